@@ -1,0 +1,208 @@
+"""Benchmark of the MoE normal-mode hot path on one MI355X.
+
+One step = moe_layout + moe_dispatch + moe_combine over one batch of seeded
+synthetic input already resident in HBM (default: the DeepSeek-V3-shaped
+prefill, S=4096 H=7168 E=256 P=8 K=8, bf16). Prints ONE JSON line with the
+whole-step throughput in GB/s of algorithmic bytes, tokens/s, per-kernel event
+timings, the roofline of the dominant kernel and the CPU oracle timed on the
+host cores as a reported baseline.
+
+Algorithmic bytes (what the method must move; zero padding and the window
+reservation are not traffic):
+  layout   = topk_idx + is_token_in_rank + counts + slot bases + slot_idx + both prefix matrices
+  dispatch = x + slot_idx + N * (payload + 12-byte triple [+ 4-byte scale for fp8])
+  combine  = slot_idx + topk_weights + N * 2H (gathered rows) + y
+with N the number of valid (token, k) entries.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD specification
+METRIC = "dispatch+combine GB/s and tokens/s on 1 MI355X; % of HBM peak (S=4096,H=7168,K=8)"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def algorithmic_bytes(w, C, n_valid):
+    S, H, K, E, P = w.S, w.H, w.K, w.E, w.P
+    layout = 4 * S * K + S * P + 4 * (P + E) + 4 * (P + 1 + E + 1) + 4 * S * K + 4 * (P + E) * C
+    payload = 2 * H if w.quant == 0 else H
+    dispatch = 2 * S * H + 4 * S * K + n_valid * (payload + 12 + (4 if w.quant else 0))
+    combine = 4 * S * K + 4 * S * K + n_valid * 2 * H + 2 * S * H
+    return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if still current."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        rec = data.get(kernel_key)
+        if not rec:
+            return None
+        import hashlib
+
+        src = os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", rec["source"])
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None  # the kernel changed since the counters were taken
+        return rec["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, C, inp, expert_out, n_valid):
+    """The oracle as it stands, on the host cores: one full step of the same workload."""
+    import oracle
+
+    ru0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    lay = oracle.layout(inp["topk_idx"], w.E, w.P, C)
+    oracle.dispatch_slots(inp["x"], lay["slot_idx"], w.quant, 0)
+    oracle.combine(expert_out, lay["slot_idx"], inp["topk_weights"])
+    wall = time.perf_counter() - t0
+    ru1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+    total = sum(algorithmic_bytes(w, C, n_valid).values())
+    return {
+        "value": round(total / wall / 1e9, 3),
+        "unit": "GB/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"one full step (layout+dispatch+combine) of {w.describe()}, {wall:.1f} s wall, "
+                  f"{cpu:.1f} s cpu, {w.S / wall:.0f} tokens/s; host has {os.cpu_count()} logical cpus",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--channels", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the work; multi-GPU runs are not part of this "
+              "build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_moe_layout_02_amd as moe
+    from workloads import WORKLOADS, draw_expert_out, make_inputs
+
+    w = WORKLOADS[args.config]
+    C = args.channels or w.C
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = make_inputs(w, with_expert_out=False)
+    valid = (inp["topk_idx"] >= 0) & (inp["topk_idx"] < w.E)
+    n_valid = int(valid.sum())
+    eo_host = draw_expert_out(w.seed + 1000, n_valid, w.H)
+
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    topk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    wts = torch.from_numpy(inp["topk_weights"]).to(dev)
+    eo = torch.from_numpy(eo_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    lay = moe.empty_layout(w.S, w.K, w.E, w.P, C, dev)
+    window = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        moe.moe_layout(topk, w.E, w.P, C, out=lay)
+        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel events on the stream the kernels run on, inside the timed region
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        moe.moe_layout(topk, w.E, w.P, C, out=lay)
+        e[1].record(stream)
+        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+        e[2].record(stream)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms = {k: [] for k in ("layout", "dispatch", "combine")}
+    for e in ev:
+        ms["layout"].append(e[0].elapsed_time(e[1]))
+        ms["dispatch"].append(e[1].elapsed_time(e[2]))
+        ms["combine"].append(e[2].elapsed_time(e[3]))
+    nbytes = algorithmic_bytes(w, C, n_valid)
+    kernels = {}
+    for k, v in ms.items():
+        avg_us = 1e3 * float(np.mean(v))
+        gbs = nbytes[k] / (avg_us * 1e-6) / 1e9
+        kernels[k] = {
+            "avg_us": round(avg_us, 2), "min_us": round(1e3 * float(np.min(v)), 2),
+            "median_us": round(1e3 * float(np.median(v)), 2), "bytes": nbytes[k],
+            "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        }
+
+    total_bytes = sum(nbytes.values())
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
+    kernel_key = {"dispatch": "pack_fp8" if w.quant else "pack_bf16", "combine": "combine"}[dom]
+    traffic = traffic_from_profiles(f"{kernel_key}:{w.name}")
+    roofline = {
+        "bound": "hbm", "kernel": kernel_key,
+        "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(kernels[dom]["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "algorithmic_bytes_per_launch": nbytes[dom],
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3+bf16" if w.quant else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe() + f" C={C}", "S": w.S, "H": w.H, "E": w.E, "P": w.P,
+                   "K": w.K, "C": C, "quant": "fp8_e4m3_dynamic" if w.quant else "none",
+                   "seed": w.seed, "parallelism": "single GPU (P virtual ranks)"},
+        "tokens_per_s": round(w.S / (ms_per_step * 1e-3), 1),
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+"""MI355X-native MoE normal-mode layout / dispatch / combine.
+
+Thin Python binding of ``libmoe.so`` (the HIP kernels behind the C ABI of
+``include/moe.h``). Functions carry the C names; they only marshal torch tensors
+(device pointers, sizes, the current HIP stream) into the C calls, allocate
+outputs the caller did not pass, and turn negative status codes into
+exceptions. Every step of the computation runs in the library's kernels; there
+is no other code path. Importing this package fails if the library is not built
+(``python -m combine_moe_layout_02_amd.build``).
+"""
+
+import ctypes
+import os
+from typing import NamedTuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_ALIGN = -2
+MOE_ERR_WINDOW = -3
+MOE_ERR_UNSUPPORTED = -4
+MOE_ERR_HIP = -5
+
+MOE_QUANT_NONE = 0
+MOE_QUANT_FP8_E4M3_DYN = 1
+
+EXPORTED = (
+    "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
+    "moe_combine", "moe_status_string",
+)
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m combine_moe_layout_02_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation."
+        )
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "moe_slot_bytes": (I64, [I32]),
+        "moe_window_bytes": (I64, [I32, I32, I32]),
+        "moe_slot_offsets": (ctypes.c_int, [I32, I32, P, P, P, P]),
+        "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
+        "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
+        "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+class MoeError(RuntimeError):
+    """A HIP launch error reported by the library."""
+
+
+def moe_status_string(status):
+    return _lib.moe_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status == MOE_OK:
+        return
+    msg = f"{moe_status_string(status)} (status {status})"
+    if status == MOE_ERR_HIP:
+        raise MoeError(msg)
+    raise ValueError(msg)
+
+
+def _stream(dev, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_slot_bytes(H):
+    v = _lib.moe_slot_bytes(int(H))
+    if v < 0:
+        _check(int(v))
+    return int(v)
+
+
+def moe_window_bytes(S, K, H):
+    v = _lib.moe_window_bytes(int(S), int(K), int(H))
+    if v < 0:
+        _check(int(v))
+    return int(v)
+
+
+def moe_slot_offsets(H, quant=MOE_QUANT_NONE):
+    vals = [ctypes.c_int64() for _ in range(4)]
+    _check(_lib.moe_slot_offsets(int(H), int(quant), *[ctypes.byref(v) for v in vals]))
+    keys = ("payload_bytes", "scale_off", "triple_off", "tail_end")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+class Layout(NamedTuple):
+    is_token_in_rank: torch.Tensor  # bool [S, P]
+    num_tokens_per_rank: torch.Tensor  # int32 [P]
+    num_tokens_per_expert: torch.Tensor  # int32 [E]
+    rank_prefix_matrix: torch.Tensor  # int32 [P, C]
+    expert_prefix_matrix: torch.Tensor  # int32 [E, C]
+    rank_slot_base: torch.Tensor  # int32 [P + 1]
+    expert_slot_base: torch.Tensor  # int32 [E + 1]
+    slot_idx: torch.Tensor  # int32 [S, K]
+    status: torch.Tensor  # int32 [1]
+
+
+def empty_layout(S, K, E, P, C, device):
+    """Output buffers for moe_layout (allocation only)."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return Layout(
+        torch.empty((S, P), dtype=torch.bool, device=device),
+        torch.empty(P, **i32), torch.empty(E, **i32), torch.empty((P, C), **i32),
+        torch.empty((E, C), **i32), torch.empty(P + 1, **i32), torch.empty(E + 1, **i32),
+        torch.empty((S, K), **i32), torch.empty(1, **i32),
+    )
+
+
+def moe_layout(topk_idx, num_experts, num_ranks, num_channels, out=None, stream=None):
+    """Routing layout of topk_idx (int32 [S, K]) for E experts over P ranks and C channels."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    S, K = topk_idx.shape
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    dev = topk_idx.device
+    if out is None:
+        out = empty_layout(S, K, E, P, C, dev)
+    shapes = [(S, P), (P,), (E,), (P, C), (E, C), (P + 1,), (E + 1,), (S, K), (1,)]
+    for name, t, shp in zip(Layout._fields, out, shapes):
+        _need(t, name, torch.bool if name == "is_token_in_rank" else torch.int32, device=dev)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+    _check(_lib.moe_layout(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                           _stream(dev, stream)))
+    return out
+
+
+def moe_dispatch(x, slot_idx, window, quant=MOE_QUANT_NONE, src_rank=0, stream=None):
+    """Pack bf16 rows x [S, H] into the window slots named by slot_idx [S, K]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 2, x.device)
+    _need(window, "window", device=x.device)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_dispatch(_ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank),
+                             _ptr(window), nbytes, _stream(x.device, stream)))
+    return window
+
+
+def moe_combine(expert_out, slot_idx, topk_weights, row_stride_bytes=None, expert_rows=None,
+                hidden=None, y=None, stream=None):
+    """y[t] = bf16(sum_k w[t,k] * expert_out[slot_idx[t,k]]) with fp32 accumulation.
+
+    expert_out is either a bf16 [R, H] tensor (row stride 2H, R rows) or any device
+    buffer with explicit row_stride_bytes, expert_rows and hidden (for example the
+    dispatch window with row_stride_bytes = moe_slot_bytes(H)).
+    """
+    _need(slot_idx, "slot_idx", torch.int32, 2)
+    dev = slot_idx.device
+    _need(expert_out, "expert_out", device=dev)
+    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
+    S, K = slot_idx.shape
+    if tuple(topk_weights.shape) != (S, K):
+        raise ValueError("topk_weights must match slot_idx")
+    if row_stride_bytes is None:
+        if expert_out.dtype != torch.bfloat16 or expert_out.dim() != 2:
+            raise ValueError("pass row_stride_bytes/expert_rows/hidden for a non-[R, H] bf16 buffer")
+        expert_rows, H = expert_out.shape
+        row_stride_bytes = 2 * H
+    else:
+        if expert_rows is None or hidden is None:
+            raise ValueError("expert_rows and hidden are required with row_stride_bytes")
+        H = int(hidden)
+        if int(expert_rows) * int(row_stride_bytes) > expert_out.numel() * expert_out.element_size():
+            raise ValueError("expert_rows * row_stride_bytes exceeds the expert_out buffer")
+    if y is None:
+        y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (S, H):
+        raise ValueError(f"y must have shape {(S, H)}")
+    _check(_lib.moe_combine(_ptr(expert_out), int(row_stride_bytes), int(expert_rows),
+                            _ptr(slot_idx), _ptr(topk_weights), S, H, K, _ptr(y),
+                            _stream(dev, stream)))
+    return y
+
+
+__all__ = [
+    "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
+    "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MoeError", "Layout",
+    "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
+    "moe_dispatch", "moe_combine", "moe_status_string",
+]

@@ -1,0 +1,128 @@
+// C ABI of the library (declared in include/moe.h): host-side validation, then kernel launches.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues nothing and touches no
+// device state. This mirrors the host tiling step of the CAM operators, which validates shapes and
+// the window size before launching ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 8.2, whose
+// "HCCL_BUFFSIZE too SMALL" error becomes MOE_ERR_WINDOW), and the required-input errors of the
+// DeepEP Python entry ("Ascend DeepEP MoE Dispatch Optimization", section "从 Python 接口进入真实调用链").
+
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_hidden(int32_t H) {
+    if (H < 16 || H > MOE_MAX_HIDDEN) return MOE_ERR_ARG;
+    if (H % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_tokens(int32_t S, int32_t K) {
+    if (S < 1 || K < 1 || K > MOE_MAX_K) return MOE_ERR_ARG;
+    if (S > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_slot_bytes(int32_t H) {
+    const int st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    return moe::slot_geom(H, MOE_QUANT_NONE).slot_bytes;
+}
+
+int64_t moe_window_bytes(int32_t S, int32_t K, int32_t H) {
+    int st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    return (int64_t)S * K * moe::slot_geom(H, MOE_QUANT_NONE).slot_bytes;
+}
+
+int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *scale_off,
+                     int64_t *triple_off, int64_t *tail_end) {
+    const int st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_E4M3_DYN) return MOE_ERR_ARG;
+    const moe::SlotGeom g = moe::slot_geom(H, quant);
+    if (payload_bytes) *payload_bytes = g.payload_bytes;
+    if (scale_off) *scale_off = g.scale_off;
+    if (triple_off) *triple_off = g.triple_off;
+    if (tail_end) *tail_end = g.tail_end;
+    return MOE_OK;
+}
+
+int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+               uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+               int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+               int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
+               int32_t *slot_idx, int32_t *status, hipStream_t stream) {
+    if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
+        !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
+        !slot_idx || !status)
+        return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    if (E % P != 0) return MOE_ERR_UNSUPPORTED;
+    const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
+                         expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
+    for (const void *p : i32)
+        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+    return from_hip(moe::launch_layout(topk_idx, S, K, E, P, C, is_token_in_rank,
+                                       num_tokens_per_rank, num_tokens_per_expert,
+                                       rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
+                                       expert_slot_base, slot_idx, status, stream));
+}
+
+int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                 int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
+                 hipStream_t stream) {
+    if (!x || !slot_idx || !window) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_E4M3_DYN) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+}
+
+int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
+                const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
+                int32_t K, void *y, hipStream_t stream) {
+    if (!expert_out || !slot_idx || !topk_weights || !y) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (expert_rows < 0 || row_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
+    if (row_stride_bytes % 16 != 0 || !aligned(expert_out, 16) || !aligned(y, 16) ||
+        !aligned(slot_idx, 4) || !aligned(topk_weights, 4))
+        return MOE_ERR_ALIGN;
+    return from_hip(moe::launch_combine(expert_out, row_stride_bytes, expert_rows, slot_idx,
+                                        topk_weights, S, H, K, y, stream));
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument (null pointer or size out of range)";
+        case MOE_ERR_ALIGN: return "misaligned pointer or stride";
+        case MOE_ERR_WINDOW: return "window too small: need S*K*moe_slot_bytes(H) bytes";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape (E % P != 0, H % 16 != 0 or S too large)";
+        case MOE_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

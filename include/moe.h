@@ -1,0 +1,153 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE normal-mode layout / dispatch / combine library.
+ *
+ * One GPU's share of expert-parallel dispatch and combine: the P expert-parallel ranks are P
+ * contiguous partitions of one caller-owned HBM window, so nothing here talks to another GPU.
+ *
+ * Notation follows "Ascend DeepEP MoE Dispatch Optimization", section "一条 token 如何走完 MoE":
+ * x[S,H] token rows, topk_idx[S,K] and topk_weights[S,K] from the router, E global experts spread
+ * over P ranks with experts_per_rank = E / P, dst_rank = expert_id / experts_per_rank and
+ * dst_local_expert = expert_id % experts_per_rank.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers; sizes are element counts unless named *_bytes.
+ *   - All arrays are dense and row-major.
+ *   - The caller allocates and owns every buffer; the library allocates nothing, keeps no state
+ *     between calls, and is reentrant. Calls that take a stream only enqueue work on it and return
+ *     without synchronising the host.
+ *   - Arguments are validated on the host before any HIP call. On a validation failure nothing is
+ *     enqueued and a negative moe_status is returned. MOE_ERR_HIP reports a failed launch.
+ */
+#ifndef MOE_LAYOUT_MI355X_H
+#define MOE_LAYOUT_MI355X_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = -1,         /* null pointer or a size outside its documented range          */
+    MOE_ERR_ALIGN = -2,       /* a pointer or stride is not aligned as documented             */
+    MOE_ERR_WINDOW = -3,      /* window_bytes < moe_window_bytes(S, K, H)                     */
+    MOE_ERR_UNSUPPORTED = -4, /* E % P != 0, H % 16 != 0, or S above MOE_MAX_TOKENS           */
+    MOE_ERR_HIP = -5          /* the HIP runtime reported an error for a launch               */
+} moe_status;
+
+typedef enum {
+    MOE_QUANT_NONE = 0,        /* bf16 payload                                               */
+    MOE_QUANT_FP8_E4M3_DYN = 1 /* per-token E4M3FN payload + fp32 scale in the slot tail     */
+} moe_quant;
+
+/* Limits. The expert, rank and top-k bounds are those the CAM kernels check ("HCCL Window 模式
+ * (Non-SHMEM) 代码深度剖析", section 9.6 限制常量: MOE_EXPERT_MAX_NUM 512, K_MAX 16, 384 ranks). The
+ * CAM batch bound of 8000 tokens is not kept, so that S = 8192 fits; H may go below the CAM H_MIN. */
+#define MOE_MAX_K 16
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_RANKS 384
+#define MOE_MAX_CHANNELS 4096
+#define MOE_MAX_TOKENS 65536
+#define MOE_MAX_HIDDEN 16384
+
+/* Bytes of one window slot: Ceil(Ceil(2H, 32) * 32 + 44, 512) * 512, the dispatch token size of
+ * "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 8.2 (Window 大小校验): the bf16 row padded to
+ * 32 bytes, a 32-byte scale block and a 12-byte triple, rounded up to 512 bytes (14848 at H=7168).
+ * The fp8 slot has the same size. Returns a negative moe_status if H is not in [16, MOE_MAX_HIDDEN]
+ * or not a multiple of 16. */
+int64_t moe_slot_bytes(int32_t H);
+
+/* Window bytes moe_dispatch needs: S * K * moe_slot_bytes(H), room for every (token, k) copy, so
+ * the caller never reads a count back (the worst-case sizing of "Ascend DeepEP MoE Dispatch
+ * Optimization", section "输出长度有动态和固定两种模式"). Negative moe_status on bad arguments. */
+int64_t moe_window_bytes(int32_t S, int32_t K, int32_t H);
+
+/* Byte offsets inside one slot ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 2.3 数据区 Token
+ * 格式): payload [0, payload_bytes) = 2H (bf16) or H (fp8); scale block [scale_off, scale_off+32)
+ * with scale_off = Ceil(payload_bytes, 32) * 32 and the fp32 scale in its first 4 bytes (zero in
+ * bf16 mode); triple int32 (src_rank, token, k) at triple_off = scale_off + 32; zero padding up
+ * to tail_end = Ceil(triple_off + 12, 128). moe_dispatch writes exactly [0, tail_end) of each
+ * used slot. Any output pointer may be NULL. Returns MOE_OK or a negative moe_status. */
+int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *scale_off,
+                     int64_t *triple_off, int64_t *tail_end);
+
+/* Routing layout: topk_idx -> membership, counts, prefix matrices and the slot of every (t, k).
+ *
+ * Follows the dispatch handle and notify stage of "Ascend DeepEP MoE Dispatch Optimization"
+ * (sections "Dispatch handle 六项分别保存什么", "Notify 先交换数量和前缀", "Device 侧如何把 channel
+ * 变成远端 Put") and the per-expert offset + running count of the CAM pack ("HCCL Window 模式
+ * (Non-SHMEM) 代码深度剖析", section 3.6 InputToShare).
+ *
+ * In:  topk_idx  int32 [S, K]. Ids in [0, E) are valid; -1 is a pad; any other value is treated
+ *                as a pad and sets bit 0 of *status.
+ *      S in [1, MOE_MAX_TOKENS], K in [1, MOE_MAX_K], E in [1, MOE_MAX_EXPERTS],
+ *      P in [1, MOE_MAX_RANKS] with E % P == 0, C (channels) in [1, min(S, MOE_MAX_CHANNELS)].
+ *      Channel c owns tokens [c*(S/C) + min(c, S%C), ...) with S/C + (c < S%C) tokens
+ *      ("HCCL Window 模式", section 8.3 分片策略).
+ * Out (all fully overwritten):
+ *      is_token_in_rank      uint8 [S, P]  1 iff token t has a valid expert on rank r
+ *      num_tokens_per_rank   int32 [P]     tokens routed to each rank (a token counts once)
+ *      num_tokens_per_expert int32 [E]     valid (t, k) entries per expert
+ *      rank_prefix_matrix    int32 [P, C]  tokens of channels 0..c routed to rank r (inclusive)
+ *      expert_prefix_matrix  int32 [E, C]  entries of channels 0..c routed to expert e (inclusive)
+ *      rank_slot_base        int32 [P+1]   first slot of rank r; [P] = N, the valid-entry count
+ *      expert_slot_base      int32 [E+1]   first slot of expert e; [E] = N
+ *      slot_idx              int32 [S, K]  slot of (t, k), or -1 for pads. Slots are ordered by
+ *                                          expert id, then source token, then k, so each rank's
+ *                                          slots are the contiguous range
+ *                                          [rank_slot_base[r], rank_slot_base[r+1]).
+ *      status                int32 [1]     0, or bit 0 set if an id outside [-1, E) was seen
+ * Enqueues three kernels on `stream`. No output may alias an input or another output. */
+int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+               uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+               int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+               int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
+               int32_t *slot_idx, int32_t *status, hipStream_t stream);
+
+/* Dispatch pack: for every (t, k) with slot s = slot_idx[t, k] >= 0, write slot s of the window
+ * (byte offset s * moe_slot_bytes(H)) as the slot layout above: the bf16 row x[t], or its
+ * per-token E4M3FN quantisation (amax over the row, scale = amax / 448 in fp32, codes =
+ * E4M3FN(x / scale) rounded to nearest even and saturated; an all-zero row gives scale 0 and zero
+ * codes), then the scale block and the triple (src_rank, t, k). This is the CAM InputToShare copy
+ * with its DynamicQuant branch ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 and the
+ * slot format of section 2.3), with each row read once per token instead of once per copy.
+ *
+ * In:  x        bf16 [S, H] as raw 16-bit words, 16-byte aligned.
+ *      slot_idx int32 [S, K] from moe_layout (or any table of distinct slots); entries < 0 and
+ *               entries >= S * K are skipped.
+ *      H in [16, MOE_MAX_HIDDEN], H % 16 == 0; quant is a moe_quant; src_rank is stored verbatim.
+ *      window   512-byte aligned device buffer of window_bytes >= moe_window_bytes(S, K, H).
+ * Writes bytes [0, tail_end) of each used slot and nothing else. Slots nobody maps to, and
+ * the bytes after tail_end in every slot, keep their contents. */
+int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                 int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
+                 hipStream_t stream);
+
+/* Combine: y[t] = bf16( sum over k = 0..K-1 ascending with slot_idx[t, k] valid of
+ *                       fp32(topk_weights[t, k] * fp32(expert_out row slot_idx[t, k])) ),
+ * accumulated in fp32 from +0.0, each product and each sum rounded to fp32 (no fused
+ * multiply-add), one round-to-nearest-even to bf16 at the end; a token with no valid entry gives
+ * +0.0. This is ReadBufferAndWeightedSum of "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 7.8,
+ * with the K rows gathered by slot index instead of first scattered to position t*K + k.
+ *
+ * In:  expert_out    bf16 rows, row r at byte offset r * row_stride_bytes; 16-byte aligned;
+ *                    row_stride_bytes >= 2H and a multiple of 16. Passing the window with
+ *                    row_stride_bytes = moe_slot_bytes(H) combines the dispatched bf16 payload.
+ *      expert_rows   number of readable rows; entries of slot_idx outside [0, expert_rows) are
+ *                    skipped like pads.
+ *      slot_idx      int32 [S, K]; topk_weights fp32 [S, K].
+ * Out: y             bf16 [S, H], 16-byte aligned, fully overwritten; must not overlap the inputs. */
+int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
+                const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
+                int32_t K, void *y, hipStream_t stream);
+
+/* Static description of a moe_status value (never NULL). */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYOUT_MI355X_H */

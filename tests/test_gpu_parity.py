@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle.
+
+Bar: layout, slot indices and dispatched bytes bit-exact; fp8 codes and scales
+exact (they are part of the dispatched bytes); combine within 1 bf16 ulp
+(|err| <= 2^-7 |ref|), and expected bit-exact since both sides round the same
+fp32 mul-then-add sequence once. Inputs are the seeded workloads at full size
+with the bench's channel count, plus tiny adversarial tables. Windows and
+outputs are poisoned before each call so unwritten bytes show up.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, draw_expert_out, f32_to_bf16_input, make_inputs, random_tiny_routing
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+POISON = 0xAB
+LAYOUT_KEYS = [
+    "is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_expert", "rank_prefix_matrix",
+    "expert_prefix_matrix", "rank_slot_base", "expert_slot_base", "slot_idx",
+]
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import combine_moe_layout_02_amd as m
+
+    return m
+
+
+@functools.lru_cache(maxsize=None)
+def inputs(cfg):
+    """x, topk_idx, topk_weights of a workload (kept for the whole module)."""
+    return make_inputs(WORKLOADS[cfg], with_expert_out=False)
+
+
+@functools.lru_cache(maxsize=1)
+def expert_out(cfg):
+    w = WORKLOADS[cfg]
+    return draw_expert_out(w.seed + 1000, w.S * w.K, w.H)
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_dev(bits):
+    return to_dev(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def poisoned_layout(moe, S, K, E, P, C):
+    out = moe.empty_layout(S, K, E, P, C, DEV)
+    for t in out:
+        t.view(torch.uint8).fill_(POISON)
+    return out
+
+
+def gpu_layout(moe, idx, E, P, C):
+    S, K = idx.shape
+    lay = moe.moe_layout(to_dev(idx), E, P, C, out=poisoned_layout(moe, S, K, E, P, C))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in lay._asdict().items()}
+
+
+def assert_layout_equal(got, ref, what=""):
+    for key in LAYOUT_KEYS:
+        g = got[key].astype(np.uint8) if key == "is_token_in_rank" else got[key]
+        if not np.array_equal(g, ref[key]):
+            bad = np.argwhere(g != ref[key])[:5]
+            raise AssertionError(f"{what} {key} differs at {bad.tolist()}")
+    assert int(got["status"][0]) == ref["status"], what
+
+
+def gpu_dispatch(moe, x_bits, slot, quant, src_rank=0):
+    S, H = x_bits.shape
+    K = slot.shape[1]
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(bf16_dev(x_bits), to_dev(slot), win, quant, src_rank)
+    torch.cuda.synchronize()
+    return win.cpu().numpy().reshape(S * K, -1)
+
+
+def assert_window_equal(win, ref_regions, geom, what=""):
+    n = ref_regions.shape[0]
+    got = win[:n, : geom.tail_end]
+    if not np.array_equal(got, ref_regions):
+        s, b = np.argwhere(got != ref_regions)[0]
+        raise AssertionError(f"{what} slot {s} byte {b}: gpu {got[s, b]:#x} oracle {ref_regions[s, b]:#x}")
+    assert np.all(win[:n, geom.tail_end:] == POISON), f"{what} wrote past tail_end"
+    assert np.all(win[n:] == POISON), f"{what} wrote an unused slot"
+
+
+def gpu_combine(moe, rows_bits, slot, w):
+    y = moe.moe_combine(bf16_dev(rows_bits), to_dev(slot), to_dev(w))
+    torch.cuda.synchronize()
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_within_ulp(got, ref, what=""):
+    g = oracle.bf16_bits_to_f32(got).astype(np.float64)
+    r = oracle.bf16_bits_to_f32(ref).astype(np.float64)
+    err = np.abs(g - r)
+    ok = err <= np.abs(r) * 2.0**-7
+    if not ok.all():
+        i = np.argwhere(~ok)[0]
+        raise AssertionError(f"{what} at {i.tolist()}: gpu {g[tuple(i)]} oracle {r[tuple(i)]}")
+
+
+# ---------------------------------------------------------------- layout
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_layout_workloads(moe, cfg):
+    w = WORKLOADS[cfg]
+    idx = inputs(cfg)["topk_idx"]
+    for C in sorted({w.C, 1, 3, min(w.S, 4096)}):
+        note(f"layout cfg{cfg} {w.describe()} C={C}")
+        assert_layout_equal(gpu_layout(moe, idx, w.E, w.P, C), oracle.layout(idx, w.E, w.P, C),
+                            f"cfg{cfg} C={C}")
+
+
+TINY_LAYOUTS = [
+    # (S, K, E, P, C, p_mask, p_bad, seed)
+    (1, 1, 1, 1, 1, 0.0, 0.0, 1),
+    (5, 3, 6, 3, 2, 0.3, 0.0, 2),
+    (37, 4, 12, 4, 3, 0.2, 0.1, 3),       # bad ids -> status bit 0
+    (300, 16, 512, 1, 7, 0.1, 0.0, 4),    # K_MAX, E_MAX, one rank
+    (257, 2, 384, 384, 257, 0.0, 0.0, 5),  # P_MAX, one expert per rank, C = S
+    (1000, 8, 64, 8, 1, 0.05, 0.0, 6),    # one channel, many chunks
+    (600, 6, 5, 5, 600, 0.5, 0.02, 7),    # heavy masking, duplicate-prone
+]
+
+
+@pytest.mark.parametrize("case", TINY_LAYOUTS)
+def test_layout_tiny_adversarial(moe, case):
+    S, K, E, P, C, p_mask, p_bad, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
+    note(f"layout tiny {case}")
+    assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), str(case))
+
+
+def test_layout_special_tables(moe):
+    S, K, E, P = 96, 4, 16, 4
+    cases = {
+        "all_masked": np.full((S, K), -1, np.int32),
+        "one_expert": np.full((S, K), 5, np.int32),  # every entry to expert 5, duplicates in rows
+        "empty_experts": np.tile(np.array([0, 1, 14, 15], np.int32), (S, 1)),
+    }
+    for name, idx in cases.items():
+        for C in (1, 3, S):
+            note(f"layout special {name} C={C}")
+            assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), name)
+
+
+# ---------------------------------------------------------------- dispatch
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_dispatch_workloads(moe, cfg):
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    note(f"dispatch cfg{cfg} {w.describe()}")
+    win = gpu_dispatch(moe, inp["x"], slot, w.quant)
+    ref = oracle.dispatch_slots(inp["x"], slot, w.quant, 0)
+    assert_window_equal(win, ref, oracle.slot_geometry(w.H, w.quant), f"cfg{cfg}")
+
+
+def test_dispatch_fp8_on_bf16_workload(moe):
+    """The fp8 pack on the plain N(0,1) prefill rows as well."""
+    w = WORKLOADS[3]
+    inp = inputs(3)
+    slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    note("dispatch fp8 on cfg3 rows")
+    win = gpu_dispatch(moe, inp["x"], slot, 1)
+    assert_window_equal(win, oracle.dispatch_slots(inp["x"], slot, 1, 0),
+                        oracle.slot_geometry(w.H, 1), "fp8 cfg3")
+
+
+TINY_DISPATCH = [
+    # (S, K, H, E, P, quant, seed)
+    (1, 1, 16, 1, 1, 0, 1),
+    (1, 1, 16, 1, 1, 1, 2),
+    (9, 3, 48, 6, 3, 1, 3),        # fp8 payload 48 B: 16-byte pad before the scale block
+    (33, 5, 2064, 10, 5, 0, 4),    # H not a multiple of the workgroup's vector stride
+    (33, 5, 2064, 10, 5, 1, 5),
+    (6, 16, 16384, 32, 4, 0, 6),   # MOE_MAX_HIDDEN, K_MAX
+    (6, 16, 16384, 32, 4, 1, 7),
+    (70, 2, 1024, 4, 2, 1, 8),
+]
+
+
+@pytest.mark.parametrize("case", TINY_DISPATCH)
+def test_dispatch_tiny(moe, case):
+    S, K, H, E, P, quant, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=0.2)
+    x = rng.standard_normal((S, H)).astype(np.float32) * 4
+    x[0, :] = 0.0  # an all-zero row: fp8 scale 0, codes 0
+    if S > 2:
+        x[1, 3] = 1e4  # an outlier
+        x[2, :] = -0.0
+    xb = f32_to_bf16_input(x)
+    slot = oracle.layout(idx, E, P, 1)["slot_idx"]
+    note(f"dispatch tiny {case}")
+    win = gpu_dispatch(moe, xb, slot, quant, src_rank=seed)
+    assert_window_equal(win, oracle.dispatch_slots(xb, slot, quant, seed),
+                        oracle.slot_geometry(H, quant), str(case))
+
+
+def test_dispatch_all_masked_writes_nothing(moe):
+    S, K, H = 8, 4, 64
+    slot = np.full((S, K), -1, np.int32)
+    xb = f32_to_bf16_input(np.ones((S, H), np.float32))
+    for quant in (0, 1):
+        win = gpu_dispatch(moe, xb, slot, quant)
+        assert np.all(win == POISON)
+
+
+# ---------------------------------------------------------------- combine
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_combine_workloads(moe, cfg):
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    note(f"combine cfg{cfg} {w.describe()}")
+    eo = expert_out(cfg)
+    got = gpu_combine(moe, eo, slot, inp["topk_weights"])
+    ref = oracle.combine(eo, slot, inp["topk_weights"])
+    assert_bf16_within_ulp(got, ref, f"cfg{cfg}")
+    assert np.array_equal(got, ref), f"cfg{cfg}: within 1 ulp but not bit-exact"
+
+
+TINY_COMBINE = [
+    # (S, K, H, R, p_mask, seed)
+    (1, 1, 16, 1, 0.0, 1),
+    (17, 3, 48, 60, 0.3, 2),
+    (40, 16, 2064, 700, 0.1, 3),
+    (5, 8, 16384, 40, 0.2, 4),
+    (64, 2, 1024, 128, 1.0, 5),  # everything masked -> +0.0
+]
+
+
+@pytest.mark.parametrize("case", TINY_COMBINE)
+def test_combine_tiny(moe, case):
+    S, K, H, R, p_mask, seed = case
+    rng = np.random.default_rng(seed)
+    slot = np.stack([rng.choice(R, size=K, replace=K > R) for _ in range(S)]).astype(np.int32)
+    slot[rng.random((S, K)) < p_mask] = -1
+    rows = f32_to_bf16_input(rng.standard_normal((R, H)).astype(np.float32) * 3)
+    w = rng.standard_normal((S, K)).astype(np.float32)
+    note(f"combine tiny {case}")
+    got = gpu_combine(moe, rows, slot, w)
+    ref = oracle.combine(rows, slot, w)
+    assert_bf16_within_ulp(got, ref, str(case))
+    assert np.array_equal(got, ref), f"{case}: within 1 ulp but not bit-exact"
+
+
+def test_combine_from_window_round_trip(moe):
+    """Identity experts: combine read straight from the bf16 window returns x (weights sum to 1)."""
+    w = WORKLOADS[3]
+    inp = inputs(3)
+    x = bf16_dev(inp["x"])
+    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
+    win = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(x, lay.slot_idx, win, 0)
+    wts = to_dev(inp["topk_weights"])
+    y = moe.moe_combine(win, lay.slot_idx, wts, row_stride_bytes=moe.moe_slot_bytes(w.H),
+                        expert_rows=w.S * w.K, hidden=w.H)
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    slot = lay.slot_idx.cpu().numpy()
+    rows = win.cpu().numpy().reshape(w.S * w.K, -1)[:, : 2 * w.H].copy().view(np.uint16)
+    assert np.array_equal(got, oracle.combine(rows, slot, inp["topk_weights"]))
+    xr = oracle.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    assert np.all(np.abs(oracle.bf16_bits_to_f32(got) - xr) <= np.abs(xr) * 2.0**-7)
+
+
+# ---------------------------------------------------------------- determinism
+
+
+def test_repeat_runs_are_byte_identical(moe):
+    """Each kernel twice on identical inputs, outputs poisoned differently before each run."""
+    w = WORKLOADS[3]
+    inp = inputs(3)
+    idx = to_dev(inp["topk_idx"])
+    x = bf16_dev(inp["x"])
+    eo = bf16_dev(expert_out(3))
+    wts = to_dev(inp["topk_weights"])
+    outs = []
+    for poison in (0x00, 0xFF):
+        lay = moe.empty_layout(w.S, w.K, w.E, w.P, w.C, DEV)
+        for t in lay:
+            t.view(torch.uint8).fill_(poison)
+        moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
+        win = torch.full((moe.moe_window_bytes(w.S, w.K, w.H),), poison, dtype=torch.uint8, device=DEV)
+        moe.moe_dispatch(x, lay.slot_idx, win, 0)
+        y = torch.full((w.S, w.H), float(poison), dtype=torch.bfloat16, device=DEV)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        torch.cuda.synchronize()
+        g = oracle.slot_geometry(w.H, 0)
+        regions = win.view(w.S * w.K, -1)[:, : g.tail_end].cpu().numpy()
+        outs.append(([t.cpu().numpy() for t in lay], regions, y.view(torch.int16).cpu().numpy()))
+    (l0, r0, y0), (l1, r1, y1) = outs
+    for a, b in zip(l0, l1):
+        assert np.array_equal(a, b)
+    assert np.array_equal(r0, r1)
+    assert np.array_equal(y0, y1)
+
+
+def test_python_layer_rejects_bad_window(moe):
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    slot = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
+    small = torch.empty(moe.moe_window_bytes(4, 2, 64) - 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError, match="window"):
+        moe.moe_dispatch(x, slot, small)
