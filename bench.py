@@ -18,6 +18,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import resource
@@ -92,6 +93,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--channels", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="independent input sets cycled over the steps (1 = the same batch every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -115,30 +118,42 @@ def main():
     n_valid = int(valid.sum())
     eo_host = draw_expert_out(w.seed + 1000, n_valid, w.H)
 
-    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
-    topk = torch.from_numpy(inp["topk_idx"]).to(dev)
-    wts = torch.from_numpy(inp["topk_weights"]).to(dev)
-    eo = torch.from_numpy(eo_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # input sets: set 0 is the seeded workload; further sets (for --rotate) use other seeds of the
+    # same distribution so that a step's inputs are not left in the caches by the previous step
+    sets = [(to_dev(inp["x"]), torch.from_numpy(inp["topk_idx"]).to(dev),
+             torch.from_numpy(inp["topk_weights"]).to(dev), to_dev(eo_host))]
+    for j in range(1, max(1, args.rotate)):
+        wj = dataclasses.replace(w, seed=w.seed + 7919 * j)
+        ij = make_inputs(wj, with_expert_out=False)
+        if int(((ij["topk_idx"] >= 0) & (ij["topk_idx"] < w.E)).sum()) != n_valid:
+            raise RuntimeError("rotated input sets must have the same number of valid entries")
+        sets.append((to_dev(ij["x"]), torch.from_numpy(ij["topk_idx"]).to(dev),
+                     torch.from_numpy(ij["topk_weights"]).to(dev),
+                     to_dev(draw_expert_out(wj.seed + 1000, n_valid, w.H))))
     lay = moe.empty_layout(w.S, w.K, w.E, w.P, C, dev)
     window = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=dev)
     y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(i):
+        x, topk, wts, eo = sets[i % len(sets)]
         moe.moe_layout(topk, w.E, w.P, C, out=lay)
         moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # per-kernel events on the stream the kernels run on, inside the timed region
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         e = ev[i]
+        x, topk, wts, eo = sets[i % len(sets)]
         e[0].record(stream)
         moe.moe_layout(topk, w.E, w.P, C, out=lay)
         e[1].record(stream)
@@ -192,7 +207,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.describe() + f" C={C}", "S": w.S, "H": w.H, "E": w.E, "P": w.P,
                    "K": w.K, "C": C, "quant": "fp8_e4m3_dynamic" if w.quant else "none",
-                   "seed": w.seed, "parallelism": "single GPU (P virtual ranks)"},
+                   "seed": w.seed, "input_sets": len(sets),
+                   "parallelism": "single GPU (P virtual ranks)"},
         "tokens_per_s": round(w.S / (ms_per_step * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernels": kernels,

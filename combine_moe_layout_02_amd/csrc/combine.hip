@@ -6,19 +6,28 @@
 // -ffp-contract=off, so each product and sum is rounded to fp32 on its own, as the separate
 // Muls / Add steps on the page do.
 //
-// One workgroup per token. The K gathered rows are contiguous runs of 2H bytes; consecutive lanes
-// read consecutive 16-byte vectors of each row, and all K loads of a vector position are issued
-// before any arithmetic so K x 16 bytes per lane are in flight. Slots and weights are uniform per
-// workgroup and live in scalar registers.
+// Each token row is split into parts of 64 16-byte vectors and one single-wave workgroup owns one
+// (token, part): each lane issues its K gathered 16-byte loads back to back, then reduces them and
+// stores one 16-byte vector of y. Slots and weights are uniform per workgroup and live in scalar
+// registers. The gathered rows are read exactly once, so they are loaded with the non-temporal
+// policy and do not displace reusable data from the caches; y is stored with the sc0 sc1 policy.
+// Each gathered row gets its own buffer descriptor whose range is the row, so an out-of-range
+// offset reads zero instead of faulting.
 
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPartThreads = 64;
+constexpr int kLoadPolicy = 2;        // nt
+constexpr int kStorePolicy = 1 | 16;  // sc0 sc1
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
 
 __device__ inline uint32_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -26,80 +35,68 @@ __device__ inline uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int MAXV, int KMAX>
-__global__ __launch_bounds__(kThreads) void combine_kernel(
+// grid = S * nparts; workgroup (t, q) produces vectors [64q, 64q + 64) of y[t].
+template <int KMAX>
+__global__ __launch_bounds__(kPartThreads) void combine_kernel(
     const uint8_t *__restrict__ expert_out, int64_t stride, int64_t rows,
     const int32_t *__restrict__ slot_idx, const float *__restrict__ weights, int K, int nvec,
-    u32x4 *__restrict__ y) {
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    int64_t off[KMAX];
+    int nparts, uint8_t *__restrict__ y) {
+    const int t = blockIdx.x / nparts;
+    const int q = blockIdx.x - t * nparts;
+    const int v = q * kPartThreads + threadIdx.x;
+    const int row_bytes = nvec << 4;
+    __amdgpu_buffer_rsrc_t src[KMAX];
     float wk[KMAX];
     bool live[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         live[k] = false;
-        off[k] = 0;
         wk[k] = 0.0f;
+        src[k] = rsrc(expert_out, 0);
         if (k < K) {
             const int64_t s = slot_idx[(int64_t)t * K + k];
             if (s >= 0 && s < rows) {
                 live[k] = true;
-                off[k] = s * stride;
+                src[k] = rsrc(expert_out + s * stride, row_bytes);
                 wk[k] = weights[(int64_t)t * K + k];
             }
         }
     }
-    u32x4 *dst = y + (int64_t)t * nvec;
+    if (v >= nvec) return;
+    u32x4 xv[KMAX];
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-        const int v = tid + j * kThreads;
-        if (v < nvec) {
-            u32x4 xv[KMAX];
+    for (int k = 0; k < KMAX; ++k)
+        if (live[k]) xv[k] = __builtin_amdgcn_raw_buffer_load_b128(src[k], v << 4, 0, kLoadPolicy);
+    float acc[8];
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (live[k])
-                    xv[k] = *reinterpret_cast<const u32x4 *>(expert_out + off[k] + ((int64_t)v << 4));
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (live[k]) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float lo = __uint_as_float(xv[k][w] << 16);
+                const float hi = __uint_as_float(xv[k][w] & 0xFFFF0000u);
+                acc[2 * w] = acc[2 * w] + wk[k] * lo;
+                acc[2 * w + 1] = acc[2 * w + 1] + wk[k] * hi;
             }
-            float acc[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (live[k]) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float lo = __uint_as_float(xv[k][w] << 16);
-                        const float hi = __uint_as_float(xv[k][w] & 0xFFFF0000u);
-                        acc[2 * w] = acc[2 * w] + wk[k] * lo;
-                        acc[2 * w + 1] = acc[2 * w + 1] + wk[k] * hi;
-                    }
-                }
-            }
-            u32x4 out;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = bf16_rne(acc[2 * w]) | (bf16_rne(acc[2 * w + 1]) << 16);
-            dst[v] = out;
         }
     }
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[w] = bf16_rne(acc[2 * w]) | (bf16_rne(acc[2 * w + 1]) << 16);
+    const __amdgpu_buffer_rsrc_t dst = rsrc(y + (int64_t)t * row_bytes, row_bytes);
+    __builtin_amdgcn_raw_buffer_store_b128(out, dst, v << 4, 0, kStorePolicy);
 }
 
-template <int MAXV, int KMAX>
+template <int KMAX>
 hipError_t launch(const void *expert_out, int64_t stride, int64_t rows, const int32_t *slot_idx,
                   const float *weights, int S, int K, int nvec, void *y, hipStream_t stream) {
-    hipLaunchKernelGGL((combine_kernel<MAXV, KMAX>), dim3(S), dim3(kThreads), 0, stream,
-                       static_cast<const uint8_t *>(expert_out), stride, rows, slot_idx, weights, K,
-                       nvec, static_cast<u32x4 *>(y));
+    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+    hipLaunchKernelGGL((combine_kernel<KMAX>), dim3((uint32_t)S * nparts), dim3(kPartThreads), 0,
+                       stream, static_cast<const uint8_t *>(expert_out), stride, rows, slot_idx,
+                       weights, K, nvec, nparts, static_cast<uint8_t *>(y));
     return hipGetLastError();
-}
-
-template <int MAXV>
-hipError_t launch_k(const void *expert_out, int64_t stride, int64_t rows, const int32_t *slot_idx,
-                    const float *weights, int S, int K, int nvec, void *y, hipStream_t stream) {
-    if (K <= 2) return launch<MAXV, 2>(expert_out, stride, rows, slot_idx, weights, S, K, nvec, y, stream);
-    if (K <= 4) return launch<MAXV, 4>(expert_out, stride, rows, slot_idx, weights, S, K, nvec, y, stream);
-    if (K <= 8) return launch<MAXV, 8>(expert_out, stride, rows, slot_idx, weights, S, K, nvec, y, stream);
-    return launch<MAXV, 16>(expert_out, stride, rows, slot_idx, weights, S, K, nvec, y, stream);
 }
 
 }  // namespace
@@ -108,11 +105,10 @@ hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int6
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,
                           int32_t H, int32_t K, void *y, hipStream_t stream) {
     const int nvec = H / 8;
-    const int per = (nvec + kThreads - 1) / kThreads;
-    if (per <= 1) return launch_k<1>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
-    if (per <= 2) return launch_k<2>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
-    if (per <= 4) return launch_k<4>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
-    return launch_k<8>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
+    if (K <= 2) return launch<2>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
+    if (K <= 4) return launch<4>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
+    if (K <= 8) return launch<8>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
+    return launch<16>(expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, K, nvec, y, stream);
 }
 
 }  // namespace moe

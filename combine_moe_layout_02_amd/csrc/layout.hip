@@ -4,18 +4,22 @@
 // Optimization" (section "Dispatch handle 六项分别保存什么": is_token_in_rank, rank / channel prefix
 // matrices) plus the slot of every (token, k): the per-expert offset + running count of the CAM
 // pack ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 InputToShare), resolved before any
-// byte moves so the pack is a pure scatter.
+// byte moves so the pack is a pure scatter. Counts and prefix sums follow the notify stage of the
+// same DeepEP page ("Notify 先交换数量和前缀") and "internode.cu" section 1 notify_dispatch.
 //
-// Three launches on one stream:
-//   count  one workgroup per channel. LDS histograms of ranks (a rank counted once per token) and
-//          experts, the token rows of is_token_in_rank, and for each valid entry its rank among the
-//          channel's entries of the same expert in (t, k) order. That rank comes from per-wave LDS
-//          lane masks + popcount, so atomics only build masks and counts and never decide an order.
-//          Raw counts go to column c of both prefix matrices.
-//   scan   one wave per matrix row: in-place inclusive scan along the channels.
+// Three launches on one stream, each built around a single round trip to memory:
+//   count  one workgroup per channel. Lanes map to (token, k) with a power-of-two lane group per
+//          token, in (t, k) order. Per batch: a rank is counted once per token (a lane counts it
+//          only if no lower lane of its token has the same rank, compared with DPP row shifts);
+//          per-wave LDS lane masks + popcount give each entry its rank among the channel's earlier
+//          entries of the same expert (atomics build masks and counts, never an order, so the
+//          result is deterministic); the token rows of is_token_in_rank are assembled in LDS and
+//          written as words. Raw counts go to column c of both prefix matrices.
+//   scan   one wave per matrix row: all of the row is loaded first, then scanned along the channels
+//          in place (inclusive).
 //   assign one workgroup per channel: exclusive scan of the per-expert totals (the slot bases), then
 //          slot = base[e] + prefix[e][c-1] + local rank. Workgroup 0 also writes the count vectors.
-// Everything is derived from the K ids of each token, so no pass scans the [S, P] matrix.
+// Nothing scans the [S, P] matrix: everything is derived from the K ids of each token.
 
 #include "moe_internal.h"
 
@@ -25,6 +29,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRankWords = (MOE_MAX_RANKS + 31) / 32;
+constexpr int kScanRegs = 16;  // row chunks of 64 held in registers by the scan (C <= 1024 in one go)
 
 __device__ inline void channel_range(int S, int C, int c, int &begin, int &end) {
     // floor share + remainder to the first channels ("HCCL Window 模式", section 8.3 分片策略)
@@ -42,115 +47,121 @@ __device__ inline int wave_inclusive_scan(int v, int lane) {
     return v;
 }
 
+// True iff rank r (>= 0) differs from the ranks held by the lk lanes just below this one, which
+// are the lower lanes of the same token (a token's KP lanes never straddle a 16-lane DPP row).
+// Every shifted value is computed on all lanes; only bitwise ops combine them.
+template <int KP, int J = 1>
+__device__ inline bool no_lower_match(int r, int lk) {
+    if constexpr (J >= KP) {
+        return true;
+    } else {
+        // row_shr:J -> value of lane (lane - J) within the 16-lane row; -2 where there is none
+        const int rj = __builtin_amdgcn_update_dpp(-2, r, 0x110 + J, 0xF, 0xF, false);
+        return !((J <= lk) & (rj == r)) & no_lower_match<KP, J + 1>(r, lk);
+    }
+}
+
+template <int KP>
+__device__ inline bool first_in_token(int r, int lk) {
+    return (r >= 0) & no_lower_match<KP>(r, lk);
+}
+
+template <int KP>
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(
     const int32_t *__restrict__ topk, int S, int K, int E, int P, int epr, int C,
     uint8_t *__restrict__ is_in, int32_t *__restrict__ rank_prefix,
     int32_t *__restrict__ expert_prefix, int32_t *__restrict__ slot_local) {
-    __shared__ uint32_t rank_bits[kThreads][kRankWords];
+    constexpr int kTokWave = 64 / KP;             // tokens per wave per batch
+    constexpr int kTokBatch = kWaves * kTokWave;  // tokens per batch
+    __shared__ uint32_t row_bits[kTokBatch][kRankWords];
     __shared__ int32_t rank_cnt[MOE_MAX_RANKS];
     __shared__ int32_t expert_run[MOE_MAX_EXPERTS];
     __shared__ unsigned long long lane_mask[kWaves][MOE_MAX_EXPERTS];
 
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tl = wave * kTokWave + lane / KP;  // token of this lane within the batch
+    const int lk = lane % KP;                    // k of this lane
     int tb, te;
     channel_range(S, C, c, tb, te);
 
+    const int nwords = (P + 31) >> 5;
     for (int i = tid; i < P; i += kThreads) rank_cnt[i] = 0;
     for (int i = tid; i < E; i += kThreads) {
         expert_run[i] = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) lane_mask[w][i] = 0ull;
     }
-    __syncthreads();
+    for (int i = tid; i < kTokBatch * nwords; i += kThreads) row_bits[i / nwords][i % nwords] = 0u;
 
-    // Phase A: one thread per token. Distinct ranks of the token -> rank histogram + row bits.
-    const int nwords = (P + 31) >> 5;
-    for (int t0 = tb; t0 < te; t0 += kThreads) {
-        const int ntok = min(kThreads, te - t0);
-        for (int w = 0; w < nwords; ++w) rank_bits[tid][w] = 0u;
-        if (tid < ntok) {
-            const int32_t *row = topk + (int64_t)(t0 + tid) * K;
-            int rr[MOE_MAX_K];
-#pragma unroll
-            for (int k = 0; k < MOE_MAX_K; ++k) {
-                rr[k] = -1;
-                if (k < K) {
-                    const int e = row[k];
-                    if (e >= 0 && e < E) rr[k] = e / epr;
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < MOE_MAX_K; ++k) {
-                bool first = rr[k] >= 0;
-#pragma unroll
-                for (int j = 0; j < k; ++j) first = first && (rr[j] != rr[k]);
-                if (first) {
-                    atomicAdd(&rank_cnt[rr[k]], 1);
-                    rank_bits[tid][rr[k] >> 5] |= 1u << (rr[k] & 31);
-                }
-            }
+    const unsigned long long lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    auto fetch = [&](int t0) {
+        const int t = t0 + tl;
+        return (t < te && lk < K) ? topk[(int64_t)t * K + lk] : -1;
+    };
+    int next = fetch(tb);
+    __syncthreads();
+    for (int t0 = tb; t0 < te; t0 += kTokBatch) {
+        const int v = next;
+        next = fetch(t0 + kTokBatch);  // prefetch the following batch
+        const int t = t0 + tl;
+        const int e = (v >= 0 && v < E) ? v : -1;
+        const int r = e >= 0 ? e / epr : -1;
+        if (first_in_token<KP>(r, lk)) {
+            atomicAdd(&rank_cnt[r], 1);
+            atomicOr(&row_bits[tl][r >> 5], 1u << (r & 31));
         }
+        if (e >= 0) atomicOr(&lane_mask[wave][e], 1ull << lane);
         __syncthreads();
-        // rows [t0, t0 + ntok) are the contiguous bytes [t0 * P, (t0 + ntok) * P)
+
+        // local rank among the channel's earlier entries of the same expert
+        bool leader = false;
+        int count = 0;
+        if (e >= 0) {
+            const unsigned long long mine = lane_mask[wave][e];
+            int earlier = 0;
+            for (int w = 0; w < wave; ++w) earlier += __popcll(lane_mask[w][e]);
+            const int below = __popcll(mine & lt_mask);
+            slot_local[(int64_t)t * K + lk] = expert_run[e] + earlier + below;
+            leader = earlier == 0 && below == 0;  // first entry of expert e in this batch
+            if (leader)
+                for (int w = 0; w < kWaves; ++w) count += __popcll(lane_mask[w][e]);
+        }
+
+        // token rows [t0, t0 + ntok) are the contiguous bytes [t0 * P, (t0 + ntok) * P)
+        const int ntok = min(kTokBatch, te - t0);
         uint8_t *dst = is_in + (int64_t)t0 * P;
         const int nbytes = ntok * P;
         if ((((uintptr_t)dst) & 3) == 0 && (nbytes & 3) == 0) {
             uint32_t *dst32 = reinterpret_cast<uint32_t *>(dst);
             for (int wd = tid; wd < (nbytes >> 2); wd += kThreads) {
-                uint32_t v = 0;
+                uint32_t val = 0;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int i = 4 * wd + b;
-                    const int tl = i / P, r = i - tl * P;
-                    v |= ((rank_bits[tl][r >> 5] >> (r & 31)) & 1u) << (8 * b);
+                    const int tk = i / P, rr = i - tk * P;
+                    val |= ((row_bits[tk][rr >> 5] >> (rr & 31)) & 1u) << (8 * b);
                 }
-                dst32[wd] = v;
+                dst32[wd] = val;
             }
         } else {
             for (int i = tid; i < nbytes; i += kThreads) {
-                const int tl = i / P, r = i - tl * P;
-                dst[i] = (uint8_t)((rank_bits[tl][r >> 5] >> (r & 31)) & 1u);
+                const int tk = i / P, rr = i - tk * P;
+                dst[i] = (uint8_t)((row_bits[tk][rr >> 5] >> (rr & 31)) & 1u);
             }
         }
         __syncthreads();
-    }
-
-    // Phase B: the channel's entries [tb*K, te*K) in (t, k) order, kThreads at a time.
-    const int64_t eb = (int64_t)tb * K, ee = (int64_t)te * K;
-    const unsigned long long lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t i0 = eb; i0 < ee; i0 += kThreads) {
-        const int64_t i = i0 + tid;
-        int e = -1;
-        if (i < ee) {
-            const int v = topk[i];
-            if (v >= 0 && v < E) e = v;
-        }
-        if (e >= 0) atomicOr(&lane_mask[wave][e], 1ull << lane);
-        __syncthreads();
-        bool leader = false;
-        int total = 0;
         if (e >= 0) {
-            const unsigned long long mine = lane_mask[wave][e];
-            int before = 0;
-            for (int w = 0; w < wave; ++w) before += __popcll(lane_mask[w][e]);
-            const int below = __popcll(mine & lt_mask);
-            slot_local[i] = expert_run[e] + before + below;
-            leader = before == 0 && below == 0;  // first entry of expert e in this batch
-            if (leader)
-                for (int w = 0; w < kWaves; ++w) total += __popcll(lane_mask[w][e]);
-        }
-        __syncthreads();
-        if (e >= 0) {
-            if (leader) expert_run[e] += total;
+            if (leader) expert_run[e] += count;
             lane_mask[wave][e] = 0ull;
         }
+        for (int i = tid; i < ntok * nwords; i += kThreads) row_bits[i / nwords][i % nwords] = 0u;
         __syncthreads();
     }
 
-    // Phase C: raw per-channel counts into column c.
+    // raw per-channel counts into column c
     for (int e = tid; e < E; e += kThreads) expert_prefix[(int64_t)e * C + c] = expert_run[e];
-    for (int r = tid; r < P; r += kThreads) rank_prefix[(int64_t)r * C + c] = rank_cnt[r];
+    for (int rr = tid; rr < P; rr += kThreads) rank_prefix[(int64_t)rr * C + c] = rank_cnt[rr];
 }
 
 __global__ __launch_bounds__(kThreads) void layout_scan_kernel(int32_t *__restrict__ expert_prefix,
@@ -164,12 +175,22 @@ __global__ __launch_bounds__(kThreads) void layout_scan_kernel(int32_t *__restri
     int32_t *row = row_id < E ? expert_prefix + (int64_t)row_id * C
                               : rank_prefix + (int64_t)(row_id - E) * C;
     int carry = 0;
-    for (int j = 0; j < C; j += 64) {
-        const bool in = j + lane < C;
-        int v = in ? row[j + lane] : 0;
-        v = wave_inclusive_scan(v, lane);
-        if (in) row[j + lane] = v + carry;
-        carry += __shfl(v, 63, 64);
+    for (int j0 = 0; j0 < C; j0 += 64 * kScanRegs) {
+        int v[kScanRegs];
+#pragma unroll
+        for (int u = 0; u < kScanRegs; ++u) {  // all loads of this stretch before any scan step
+            const int j = j0 + 64 * u + lane;
+            v[u] = j < C ? row[j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanRegs; ++u) {
+            if (j0 + 64 * u < C) {  // wave-uniform
+                const int j = j0 + 64 * u + lane;
+                const int s = wave_inclusive_scan(v[u], lane);
+                if (j < C) row[j] = s + carry;
+                carry += __shfl(s, 63, 64);
+            }
+        }
     }
 }
 
@@ -184,8 +205,18 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
 
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int tb, te;
+    channel_range(S, C, c, tb, te);
+    const int64_t eb = (int64_t)tb * K, ee = (int64_t)te * K;
 
-    // Exclusive scan of the per-expert totals (last column); thread tid owns experts 2tid, 2tid+1.
+    // first batch of the channel's entries and their local ranks, loaded up front
+    int e_cur = -1, local_cur = 0;
+    if (eb + tid < ee) {
+        e_cur = topk[eb + tid];
+        local_cur = slot_idx[eb + tid];
+    }
+
+    // exclusive scan of the per-expert totals (last column); thread tid owns experts 2tid, 2tid+1
     const int e0 = 2 * tid, e1 = 2 * tid + 1;
     const int n0 = e0 < E ? expert_prefix[(int64_t)e0 * C + C - 1] : 0;
     const int n1 = e1 < E ? expert_prefix[(int64_t)e1 * C + C - 1] : 0;
@@ -224,19 +255,30 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     }
     __syncthreads();
 
-    int tb, te;
-    channel_range(S, C, c, tb, te);
     bool bad = false;
-    for (int64_t i = (int64_t)tb * K + tid; i < (int64_t)te * K; i += kThreads) {
-        const int e = topk[i];
+    for (int64_t i = eb + tid; i < ee; i += kThreads) {
+        const int e = e_cur, local = local_cur;
+        if (i + kThreads < ee) {  // prefetch the next batch
+            e_cur = topk[i + kThreads];
+            local_cur = slot_idx[i + kThreads];
+        }
         if (e >= 0 && e < E) {
-            slot_idx[i] = off[e] + slot_idx[i];
+            slot_idx[i] = off[e] + local;
         } else {
             slot_idx[i] = -1;
             bad = bad || e != -1;
         }
     }
     if (bad) atomicOr(status, 1);
+}
+
+template <int KP>
+hipError_t launch_count(const int32_t *topk_idx, int S, int K, int E, int P, int C,
+                        uint8_t *is_in, int32_t *rank_prefix, int32_t *expert_prefix,
+                        int32_t *slot_idx, hipStream_t stream) {
+    hipLaunchKernelGGL(layout_count_kernel<KP>, dim3(C), dim3(kThreads), 0, stream, topk_idx, S, K,
+                       E, P, E / P, C, is_in, rank_prefix, expert_prefix, slot_idx);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -247,11 +289,17 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
                          int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                          int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                          hipStream_t stream) {
-    const int epr = E / P;
-    hipLaunchKernelGGL(layout_count_kernel, dim3(C), dim3(kThreads), 0, stream, topk_idx, S, K, E,
-                       P, epr, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix,
-                       slot_idx);
-    hipError_t err = hipGetLastError();
+    hipError_t err;
+    if (K <= 1)
+        err = launch_count<1>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);
+    else if (K <= 2)
+        err = launch_count<2>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);
+    else if (K <= 4)
+        err = launch_count<4>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);
+    else if (K <= 8)
+        err = launch_count<8>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);
+    else
+        err = launch_count<16>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);
     if (err != hipSuccess) return err;
     const int scan_blocks = (E + P + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(layout_scan_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream,
@@ -259,7 +307,7 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(layout_assign_kernel, dim3(C), dim3(kThreads), 0, stream, topk_idx, S, K, E,
-                       P, epr, C, expert_prefix_matrix, rank_prefix_matrix, slot_idx,
+                       P, E / P, C, expert_prefix_matrix, rank_prefix_matrix, slot_idx,
                        expert_slot_base, rank_slot_base, num_tokens_per_expert,
                        num_tokens_per_rank, status);
     return hipGetLastError();

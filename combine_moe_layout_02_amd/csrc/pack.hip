@@ -1,70 +1,80 @@
 // Dispatch pack kernels for gfx950: K-fold expanded copy of token rows into window slots.
 //
 // The CAM pack ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 InputToShare) walks the
-// (token, k) pairs and re-reads the token row for every copy. Here one workgroup owns one token:
-// the row is read from HBM once into registers (16-byte loads, consecutive lanes on consecutive
-// 16-byte vectors) and stored K times with 16-byte non-temporal stores, since the window is written
-// once and not read back by this kernel. Slot addresses come from the layout's slot_idx, so the
-// kernel is a pure scatter with no atomics. Each store stream covers whole 128-byte lines: the slot
-// pitch is a multiple of 512 bytes and the written region ends on a 128-byte boundary.
+// (token, k) pairs and re-reads the token row for every copy. Here each row is read from HBM once
+// and stored K times; slot addresses come from the layout's slot_idx, so the pack is a pure scatter
+// with no atomics.
 //
-// fp8 variant: the DynamicQuant branch of the same section (bf16 -> fp32 -> abs -> row max ->
-// scale -> narrow), with E4M3FN codes and scale = amax / 448. The row max is a wave shuffle
-// reduction followed by an LDS reduction across the workgroup's waves.
+// bf16: the row is split into parts of kPartThreads 16-byte vectors and each workgroup owns one
+// (token, part): every lane loads one vector and stores it to the K slots. Small workgroups with
+// one store per lane per slot keep the HBM write stream dense; measured on MI355X this writes
+// markedly faster than one large workgroup per token storing many vectors per lane.
+//
+// fp8: the DynamicQuant branch of the same section (bf16 -> fp32 -> abs -> row max -> scale ->
+// narrow) needs the whole row's maximum before any code is known, so one workgroup owns one token:
+// each lane holds 16 elements (one 16-byte vector of codes), the row max is a wave shuffle reduction
+// followed by an LDS reduction across waves, then codes are written to the K slots.
+//
+// Stores use buffer instructions with the sc0 sc1 nt cache policy: the window is written once and
+// not read back by this kernel, so the lines stream to HBM instead of filling L2 and the
+// memory-side cache with dirty data that later kernels would have to evict. Buffer descriptors are
+// built per slot with the slot's written size as their range, so an out-of-range offset is dropped
+// by the hardware instead of touching a neighbour.
 
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline void store_stream(void *p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+constexpr int kPartThreads = 128;   // bf16: lanes (= 16-byte vectors) per (token, part) workgroup
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyStream = 1 | 16 | 2;  // sc0 sc1 nt
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// Writes the tail of one slot: 16-byte vectors from payload_bytes to tail_end, all zero except
-// the scale vector (fp32 scale in its first word) and the triple vector (src_rank, t, k, 0).
-__device__ inline void store_tail(uint8_t *slot, const SlotGeom &g, int tid, uint32_t scale_bits,
-                                  int src_rank, int t, int k) {
-    const int ntail = (g.tail_end - g.payload_bytes) >> 4;
-    if (tid < ntail) {
-        const int off = g.payload_bytes + (tid << 4);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (off == g.scale_off) v.x = scale_bits;
-        if (off == g.triple_off) v = u32x4{(uint32_t)src_rank, (uint32_t)t, (uint32_t)k, 0u};
-        store_stream(slot + off, v);
-    }
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicyDefault);
 }
 
-// grid = S workgroups; workgroup t copies x[t] (nvec 16-byte vectors) into its K slots.
-template <int MAXV>
-__global__ __launch_bounds__(kThreads) void pack_bf16_kernel(
-    const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int nvec,
-    SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const u32x4 *src = x + (int64_t)t * nvec;
-    u32x4 row[MAXV];
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-        const int v = tid + j * kThreads;
-        if (v < nvec) row[j] = src[v];
-    }
+__device__ inline void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, int32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicyStream);
+}
+
+// Tail of one slot, lane `lane` < ntail: 16-byte vectors from payload_bytes to tail_end, all zero
+// except the scale vector (fp32 scale in its first word) and the triple vector (src_rank, t, k, 0).
+__device__ inline void store_tail(__amdgpu_buffer_rsrc_t slot, const SlotGeom &g, int lane,
+                                  uint32_t scale_bits, int src_rank, int t, int k) {
+    const int off = g.payload_bytes + (lane << 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (off == g.scale_off) v.x = scale_bits;
+    if (off == g.triple_off) v = u32x4{(uint32_t)src_rank, (uint32_t)t, (uint32_t)k, 0u};
+    store16(v, slot, off);
+}
+
+// grid = S * nparts; workgroup (t, q) copies vectors [q*kPartThreads, (q+1)*kPartThreads) of
+// x[t] into the K slots of token t; the last part also writes the slot tails.
+__global__ __launch_bounds__(kPartThreads) void pack_bf16_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int nvec,
+    int nparts, SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
+    const int t = blockIdx.x / nparts;
+    const int q = blockIdx.x - t * nparts;
+    const int lane = threadIdx.x;
+    const int v = q * kPartThreads + lane;
+    const int row_bytes = nvec << 4;
+    const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
+    const u32x4 r = load16(src, v << 4);  // out of range (v >= nvec) reads as zero, never stored
+    const bool tail_lane = q == nparts - 1 && lane < ((g.tail_end - g.payload_bytes) >> 4);
     const int32_t *slots = slot_idx + (int64_t)t * K;
     for (int k = 0; k < K; ++k) {
         const int64_t s = slots[k];
         if (s < 0 || s >= max_slots) continue;
-        uint8_t *slot = window + s * g.slot_bytes;
-#pragma unroll
-        for (int j = 0; j < MAXV; ++j) {
-            const int v = tid + j * kThreads;
-            if (v < nvec) store_stream(slot + ((int64_t)v << 4), row[j]);
-        }
-        store_tail(slot, g, tid, 0u, src_rank, t, k);
+        const __amdgpu_buffer_rsrc_t dst = rsrc(window + s * g.slot_bytes, g.tail_end);
+        if (v < nvec) store16(r, dst, v << 4);
+        if (tail_lane) store_tail(dst, g, lane, 0u, src_rank, t, k);
     }
 }
 
@@ -90,92 +100,53 @@ __device__ inline uint32_t e4m3fn_code(float q) {
     return code | sign;
 }
 
-// grid = S workgroups. Thread owns 16-element groups u = tid + j*kThreads (two 16-byte input
-// vectors each), producing one 16-byte output vector of codes per group.
-template <int MAXU>
-__global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
-    const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int ngroups,
+// Four bf16 pairs (two input words) -> four E4M3FN codes in one word, element order kept.
+__device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
+    return e4m3fn_code(bf16_lo(w0) / scale) | (e4m3fn_code(bf16_hi(w0) / scale) << 8) |
+           (e4m3fn_code(bf16_lo(w1) / scale) << 16) | (e4m3fn_code(bf16_hi(w1) / scale) << 24);
+}
+
+// grid = S; workgroup t quantises x[t]. Lane u owns elements [16u, 16u + 16): two input vectors,
+// one 16-byte output vector of codes. T >= ngroups.
+template <int T>
+__global__ __launch_bounds__(T) void pack_fp8_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int ngroups,
     SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
-    __shared__ float wave_max[kWaves];
+    __shared__ float wave_max[T / 64];
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const u32x4 *src = x + (int64_t)t * ngroups * 2;
-    u32x4 in0[MAXU], in1[MAXU];
+    const int u = threadIdx.x, lane = u & 63, wave = u >> 6;
+    const int row_bytes = ngroups << 5;
+    const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
+    const u32x4 a = load16(src, u << 5);        // elements 16u .. 16u+7 (zero past the row)
+    const u32x4 b = load16(src, (u << 5) + 16);  // elements 16u+8 .. 16u+15
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MAXU; ++j) {
-        const int u = tid + j * kThreads;
-        if (u < ngroups) {
-            in0[j] = src[2 * u];
-            in1[j] = src[2 * u + 1];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                amax = fmaxf(amax, fabsf(bf16_lo(in0[j][w])));
-                amax = fmaxf(amax, fabsf(bf16_hi(in0[j][w])));
-                amax = fmaxf(amax, fabsf(bf16_lo(in1[j][w])));
-                amax = fmaxf(amax, fabsf(bf16_hi(in1[j][w])));
-            }
-        }
+    for (int w = 0; w < 4; ++w) {
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(a[w])), fabsf(bf16_hi(a[w]))));
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(b[w])), fabsf(bf16_hi(b[w]))));
     }
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
     if (lane == 0) wave_max[wave] = amax;
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, wave_max[w]);
+    for (int w = 0; w < T / 64; ++w) amax = fmaxf(amax, wave_max[w]);
 
     const float scale = amax / 448.0f;  // IEEE round-to-nearest division
-    u32x4 codes[MAXU];
-#pragma unroll
-    for (int j = 0; j < MAXU; ++j) {
-        codes[j] = u32x4{0u, 0u, 0u, 0u};
-        const int u = tid + j * kThreads;
-        if (u < ngroups && amax > 0.0f) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t src_w = w < 2 ? in0[j][2 * w] : in1[j][2 * (w - 2)];
-                const uint32_t src_w2 = w < 2 ? in0[j][2 * w + 1] : in1[j][2 * (w - 2) + 1];
-                const uint32_t c0 = e4m3fn_code(bf16_lo(src_w) / scale);
-                const uint32_t c1 = e4m3fn_code(bf16_hi(src_w) / scale);
-                const uint32_t c2 = e4m3fn_code(bf16_lo(src_w2) / scale);
-                const uint32_t c3 = e4m3fn_code(bf16_hi(src_w2) / scale);
-                codes[j][w] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-            }
-        }
-    }
+    u32x4 codes = {0u, 0u, 0u, 0u};
+    if (u < ngroups && amax > 0.0f)
+        codes = u32x4{quant4(a[0], a[1], scale), quant4(a[2], a[3], scale),
+                      quant4(b[0], b[1], scale), quant4(b[2], b[3], scale)};
     const uint32_t scale_bits = __float_as_uint(scale);
+    const bool tail_lane = u < ((g.tail_end - g.payload_bytes) >> 4);
     const int32_t *slots = slot_idx + (int64_t)t * K;
     for (int k = 0; k < K; ++k) {
         const int64_t s = slots[k];
         if (s < 0 || s >= max_slots) continue;
-        uint8_t *slot = window + s * g.slot_bytes;
-#pragma unroll
-        for (int j = 0; j < MAXU; ++j) {
-            const int u = tid + j * kThreads;
-            if (u < ngroups) store_stream(slot + ((int64_t)u << 4), codes[j]);
-        }
-        store_tail(slot, g, tid, scale_bits, src_rank, t, k);
+        const __amdgpu_buffer_rsrc_t dst = rsrc(window + s * g.slot_bytes, g.tail_end);
+        if (u < ngroups) store16(codes, dst, u << 4);
+        if (tail_lane) store_tail(dst, g, u, scale_bits, src_rank, t, k);
     }
-}
-
-template <int MAXV>
-hipError_t launch_bf16(const void *x, const int32_t *slot_idx, int S, int K, int nvec,
-                       const SlotGeom &g, int src_rank, int64_t max_slots, void *window,
-                       hipStream_t stream) {
-    hipLaunchKernelGGL(pack_bf16_kernel<MAXV>, dim3(S), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4 *>(x), slot_idx, K, nvec, g, src_rank, max_slots,
-                       static_cast<uint8_t *>(window));
-    return hipGetLastError();
-}
-
-template <int MAXU>
-hipError_t launch_fp8(const void *x, const int32_t *slot_idx, int S, int K, int ngroups,
-                      const SlotGeom &g, int src_rank, int64_t max_slots, void *window,
-                      hipStream_t stream) {
-    hipLaunchKernelGGL(pack_fp8_kernel<MAXU>, dim3(S), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4 *>(x), slot_idx, K, ngroups, g, src_rank,
-                       max_slots, static_cast<uint8_t *>(window));
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -184,19 +155,23 @@ hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_
                        int32_t quant, int32_t src_rank, void *window, hipStream_t stream) {
     const SlotGeom g = slot_geom(H, quant);
     const int64_t max_slots = (int64_t)S * K;
+    const uint8_t *xb = static_cast<const uint8_t *>(x);
+    uint8_t *wb = static_cast<uint8_t *>(window);
     if (quant == MOE_QUANT_NONE) {
-        const int nvec = H / 8;  // 16-byte vectors of bf16
-        const int per = (nvec + kThreads - 1) / kThreads;
-        if (per <= 1) return launch_bf16<1>(x, slot_idx, S, K, nvec, g, src_rank, max_slots, window, stream);
-        if (per <= 2) return launch_bf16<2>(x, slot_idx, S, K, nvec, g, src_rank, max_slots, window, stream);
-        if (per <= 4) return launch_bf16<4>(x, slot_idx, S, K, nvec, g, src_rank, max_slots, window, stream);
-        return launch_bf16<8>(x, slot_idx, S, K, nvec, g, src_rank, max_slots, window, stream);
+        const int nvec = H / 8;  // 16-byte vectors per bf16 row
+        const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+        hipLaunchKernelGGL(pack_bf16_kernel, dim3((uint32_t)S * nparts), dim3(kPartThreads), 0,
+                           stream, xb, slot_idx, K, nvec, nparts, g, src_rank, max_slots, wb);
+        return hipGetLastError();
     }
     const int ngroups = H / 16;  // 16 elements -> one 16-byte vector of codes
-    const int per = (ngroups + kThreads - 1) / kThreads;
-    if (per <= 1) return launch_fp8<1>(x, slot_idx, S, K, ngroups, g, src_rank, max_slots, window, stream);
-    if (per <= 2) return launch_fp8<2>(x, slot_idx, S, K, ngroups, g, src_rank, max_slots, window, stream);
-    return launch_fp8<4>(x, slot_idx, S, K, ngroups, g, src_rank, max_slots, window, stream);
+    if (ngroups <= 512)
+        hipLaunchKernelGGL(pack_fp8_kernel<512>, dim3(S), dim3(512), 0, stream, xb, slot_idx, K,
+                           ngroups, g, src_rank, max_slots, wb);
+    else
+        hipLaunchKernelGGL(pack_fp8_kernel<1024>, dim3(S), dim3(1024), 0, stream, xb, slot_idx, K,
+                           ngroups, g, src_rank, max_slots, wb);
+    return hipGetLastError();
 }
 
 }  // namespace moe
