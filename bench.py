@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=1,
                     help="independent input sets cycled over the steps (1 = the same batch every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run an elementwise fp32 negate of this many MiB (reads and writes "
+                         "exactly that many bytes), to scale rocprofv3 memory counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -143,6 +146,15 @@ def main():
         moe.moe_layout(topk, w.E, w.P, C, out=lay)
         moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)
