@@ -63,27 +63,52 @@ def traffic_from_profiles(kernel_key):
         return None
 
 
-def cpu_baseline(w, C, inp, expert_out, n_valid):
-    """The oracle as it stands, on the host cores: one full step of the same workload."""
+def cpu_baseline(w, C, inp, expert_out, n_valid, min_seconds=10.0, max_reps=25):
+    """The oracle as it stands, on the host cores: full steps of the same workload, repeated
+    until about min_seconds of wall time have accumulated."""
     import oracle
 
     ru0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    lay = oracle.layout(inp["topk_idx"], w.E, w.P, C)
-    oracle.dispatch_slots(inp["x"], lay["slot_idx"], w.quant, 0)
-    oracle.combine(expert_out, lay["slot_idx"], inp["topk_weights"])
+    reps = 0
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        lay = oracle.layout(inp["topk_idx"], w.E, w.P, C)
+        oracle.dispatch_slots(inp["x"], lay["slot_idx"], w.quant, 0)
+        oracle.combine(expert_out, lay["slot_idx"], inp["topk_weights"])
+        reps += 1
     wall = time.perf_counter() - t0
     ru1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
-    total = sum(algorithmic_bytes(w, C, n_valid).values())
+    total = sum(algorithmic_bytes(w, C, n_valid).values()) * reps
     return {
         "value": round(total / wall / 1e9, 3),
         "unit": "GB/s",
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": f"one full step (layout+dispatch+combine) of {w.describe()}, {wall:.1f} s wall, "
-                  f"{cpu:.1f} s cpu, {w.S / wall:.0f} tokens/s; host has {os.cpu_count()} logical cpus",
+        "sample": f"{reps} full steps (layout+dispatch+combine) of {w.describe()}, {wall:.1f} s wall, "
+                  f"{cpu:.1f} s cpu, {reps * w.S / wall:.0f} tokens/s; host has {os.cpu_count()} logical cpus",
     }
+
+
+def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
+    """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
+    payload = 2 * w.H if w.quant == 0 else w.H
+    out = None
+    ms = []
+    for i in range(iters + 3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = moe.moe_unpack(window, lay.expert_slot_base[w.E:], w.S, w.K, w.H, w.quant, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    per_row = payload + 12 + (4 if w.quant else 0)
+    nbytes = 2 * n_valid * per_row + 4
+    avg_us = 1e3 * float(np.mean(ms))
+    return {"avg_us": round(avg_us, 2), "bytes": nbytes, "GB/s": round(nbytes / avg_us / 1e3, 1),
+            "frac_hbm_peak": round(nbytes / avg_us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -95,6 +120,10 @@ def main():
     ap.add_argument("--channels", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=1,
                     help="independent input sets cycled over the steps (1 = the same batch every step)")
+    ap.add_argument("--quant", choices=["workload", "none", "fp8", "int8"], default="workload",
+                    help="dispatch payload type (default: the workload's own)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the step (unpack of the dispatched window)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run an elementwise fp32 negate of this many MiB (reads and writes "
@@ -112,6 +141,8 @@ def main():
     from workloads import WORKLOADS, draw_expert_out, make_inputs
 
     w = WORKLOADS[args.config]
+    if args.quant != "workload":
+        w = dataclasses.replace(w, quant={"none": 0, "fp8": 1, "int8": 2}[args.quant])
     C = args.channels or w.C
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -215,10 +246,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3+bf16" if w.quant else "bf16",
+        "dtype": {0: "bf16", 1: "fp8-e4m3+bf16", 2: "int8+bf16"}[w.quant],
         "data": "synthetic",
         "config": {"workload": w.describe() + f" C={C}", "S": w.S, "H": w.H, "E": w.E, "P": w.P,
-                   "K": w.K, "C": C, "quant": "fp8_e4m3_dynamic" if w.quant else "none",
+                   "K": w.K, "C": C, "quant": {0: "none", 1: "fp8_e4m3_dynamic", 2: "int8_dynamic"}[w.quant],
                    "seed": w.seed, "input_sets": len(sets),
                    "parallelism": "single GPU (P virtual ranks)"},
         "tokens_per_s": round(w.S / (ms_per_step * 1e-3), 1),
@@ -227,6 +258,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if not args.no_extras:
+        out["extras"] = {"unpack": time_unpack(moe, torch, w, lay, window, n_valid, stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

@@ -6,7 +6,7 @@ Thin Python binding of ``libmoe.so`` (the HIP kernels behind the C ABI of
 outputs the caller did not pass, and turn negative status codes into
 exceptions. Every step of the computation runs in the library's kernels; there
 is no other code path. Importing this package fails if the library is not built
-(``python -m combine_moe_layout_02_amd.build``).
+(``python combine_moe_layout_02_amd/build.py``).
 """
 
 import ctypes
@@ -26,20 +26,25 @@ MOE_ERR_HIP = -5
 
 MOE_QUANT_NONE = 0
 MOE_QUANT_FP8_E4M3_DYN = 1
+MOE_QUANT_INT8_DYN = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
-    "moe_combine", "moe_status_string",
+    "moe_combine", "moe_unpack", "moe_status_string",
 )
 
 
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m combine_moe_layout_02_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python combine_moe_layout_02_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation."
         )
     lib = ctypes.CDLL(_LIB_PATH)
+    missing = [name for name in EXPORTED if not hasattr(lib, name)]
+    if missing:
+        raise ImportError(f"{_LIB_PATH} is stale (missing {missing}); rebuild it with "
+                          "`python combine_moe_layout_02_amd/build.py`")
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
         "moe_slot_bytes": (I64, [I32]),
@@ -48,6 +53,7 @@ def _load():
         "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
+        "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -216,9 +222,47 @@ def moe_combine(expert_out, slot_idx, topk_weights, row_stride_bytes=None, exper
     return y
 
 
+class Unpacked(NamedTuple):
+    expand_x: torch.Tensor  # [S*K, H] bf16, or uint8 codes for the quantised modes
+    expand_scales: torch.Tensor  # fp32 [S*K] (quantised modes) or None
+    expand_idx: torch.Tensor  # int32 [S*K, 3]
+
+
+def moe_unpack(window, num_slots, S, K, H, quant=MOE_QUANT_NONE, out=None, stream=None):
+    """Compact rows, triples and scales of the first N window slots (N read on the device from
+    num_slots, e.g. layout.expert_slot_base[E:]). Rows N..S*K-1 of the outputs are left as is."""
+    _need(window, "window")
+    dev = window.device
+    _need(num_slots, "num_slots", torch.int32, device=dev)
+    S, K, H, quant = int(S), int(K), int(H), int(quant)
+    rows = S * K
+    if out is None:
+        if quant == MOE_QUANT_NONE:
+            ex = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+            sc = None
+        else:
+            ex = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty(rows, dtype=torch.float32, device=dev)
+        out = Unpacked(ex, sc, torch.empty((rows, 3), dtype=torch.int32, device=dev))
+    ex, sc, idx = out
+    _need(ex, "expand_x", device=dev)
+    _need(idx, "expand_idx", torch.int32, 2, dev)
+    payload = moe_slot_offsets(H, quant)["payload_bytes"]
+    if ex.numel() * ex.element_size() < rows * payload or tuple(idx.shape) != (rows, 3):
+        raise ValueError("expand_x must hold S*K rows of payload bytes and expand_idx [S*K, 3]")
+    if sc is not None:
+        _need(sc, "expand_scales", torch.float32, device=dev)
+        if sc.numel() < rows:
+            raise ValueError("expand_scales must hold S*K values")
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_unpack(_ptr(window), nbytes, _ptr(num_slots), S, K, H, quant, _ptr(ex),
+                           None if sc is None else _ptr(sc), _ptr(idx), _stream(dev, stream)))
+    return out
+
+
 __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
-    "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MoeError", "Layout",
+    "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_combine", "moe_status_string",
+    "moe_dispatch", "moe_combine", "moe_unpack", "Unpacked", "moe_status_string",
 ]

@@ -1,7 +1,8 @@
 """Build libmoe.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Run as ``python -m combine_moe_layout_02_amd.build`` or through ``__graft_entry__.build()``.
-Always recompiles. The library lands next to this file, where the Python binding loads it.
+Run as ``python combine_moe_layout_02_amd/build.py`` (a path, so that the package, which loads
+libmoe.so at import, is not imported first) or through ``__graft_entry__.build()``. Always
+recompiles. The library lands next to this file, where the Python binding loads it.
 """
 
 import os
@@ -17,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["layout.hip", "pack.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["layout.hip", "pack.hip", "combine.hip", "unpack.hip", "moe_api.cpp"]
 
 # -ffp-contract=off: combine rounds every product and sum to fp32 on its own (no fused multiply-add).
 # -packed-fp32-ops off: scalar fp32 only; no packed fp32 instructions are generated.

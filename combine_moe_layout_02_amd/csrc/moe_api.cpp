@@ -50,7 +50,7 @@ int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *
                      int64_t *triple_off, int64_t *tail_end) {
     const int st = check_hidden(H);
     if (st != MOE_OK) return st;
-    if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_E4M3_DYN) return MOE_ERR_ARG;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
     const moe::SlotGeom g = moe::slot_geom(H, quant);
     if (payload_bytes) *payload_bytes = g.payload_bytes;
     if (scale_off) *scale_off = g.scale_off;
@@ -91,7 +91,7 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
     if (st != MOE_OK) return st;
     st = check_hidden(H);
     if (st != MOE_OK) return st;
-    if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_E4M3_DYN) return MOE_ERR_ARG;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
     if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
     if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
@@ -111,6 +111,24 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
         return MOE_ERR_ALIGN;
     return from_hip(moe::launch_combine(expert_out, row_stride_bytes, expert_rows, slot_idx,
                                         topk_weights, S, H, K, y, stream));
+}
+
+int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,
+               int32_t K, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
+               int32_t *expand_idx, hipStream_t stream) {
+    if (!window || !num_slots || !expand_x || !expand_idx) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    if (quant != MOE_QUANT_NONE && !expand_scales) return MOE_ERR_ARG;
+    if (!aligned(window, 512) || !aligned(expand_x, 16) || !aligned(num_slots, 4) ||
+        !aligned(expand_idx, 4) || (expand_scales && !aligned(expand_scales, 4)))
+        return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_unpack(window, num_slots, S, K, H, quant, expand_x, expand_scales,
+                                       expand_idx, stream));
 }
 
 const char *moe_status_string(int status) {

@@ -20,6 +20,10 @@ struct SlotGeom {
 
 constexpr int64_t ceil_to(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+inline bool valid_quant(int32_t quant) {
+    return quant == MOE_QUANT_NONE || quant == MOE_QUANT_FP8_E4M3_DYN || quant == MOE_QUANT_INT8_DYN;
+}
+
 inline SlotGeom slot_geom(int32_t H, int32_t quant) {
     SlotGeom g;
     g.slot_bytes = ceil_to(ceil_to(2 * (int64_t)H, 32) + 44, 512);
@@ -45,5 +49,9 @@ hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_
 hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,
                           int32_t H, int32_t K, void *y, hipStream_t stream);
+
+hipError_t launch_unpack(const void *window, const int32_t *num_slots, int32_t S, int32_t K,
+                         int32_t H, int32_t quant, void *expand_x, float *expand_scales,
+                         int32_t *expand_idx, hipStream_t stream);
 
 }  // namespace moe

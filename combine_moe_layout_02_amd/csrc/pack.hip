@@ -10,10 +10,11 @@
 // one store per lane per slot keep the HBM write stream dense; measured on MI355X this writes
 // markedly faster than one large workgroup per token storing many vectors per lane.
 //
-// fp8: the DynamicQuant branch of the same section (bf16 -> fp32 -> abs -> row max -> scale ->
-// narrow) needs the whole row's maximum before any code is known, so one workgroup owns one token:
-// each lane holds 16 elements (one 16-byte vector of codes), the row max is a wave shuffle reduction
-// followed by an LDS reduction across waves, then codes are written to the K slots.
+// fp8 / int8: the DynamicQuant branch of the same section (bf16 -> fp32 -> abs -> row max ->
+// scale -> narrow; the page's narrow type is INT8, E4M3FN is the second format) needs the whole
+// row's maximum before any code is known, so one workgroup owns one token: each lane holds 16
+// elements (one 16-byte vector of codes), the row max is a wave shuffle reduction followed by an
+// LDS reduction across waves, then codes are written to the K slots.
 //
 // Stores use buffer instructions with the sc0 sc1 nt cache policy: the window is written once and
 // not read back by this kernel, so the lines stream to HBM instead of filling L2 and the
@@ -100,16 +101,33 @@ __device__ inline uint32_t e4m3fn_code(float q) {
     return code | sign;
 }
 
-// Four bf16 pairs (two input words) -> four E4M3FN codes in one word, element order kept.
+// fp32 -> INT8 code (two's complement byte): round half to even, clamp to [-127, 127].
+__device__ inline uint32_t int8_code(float q) {
+    const float r = fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+    return (uint32_t)((int32_t)r) & 0xFFu;
+}
+
+template <int QUANT>
+__device__ inline uint32_t code_of(float q) {
+    if constexpr (QUANT == MOE_QUANT_FP8_E4M3_DYN) return e4m3fn_code(q);
+    else return int8_code(q);
+}
+
+// Largest code magnitude: the row's amax maps onto it.
+template <int QUANT>
+constexpr float code_max() { return QUANT == MOE_QUANT_FP8_E4M3_DYN ? 448.0f : 127.0f; }
+
+// Four bf16 pairs (two input words) -> four codes in one word, element order kept.
+template <int QUANT>
 __device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
-    return e4m3fn_code(bf16_lo(w0) / scale) | (e4m3fn_code(bf16_hi(w0) / scale) << 8) |
-           (e4m3fn_code(bf16_lo(w1) / scale) << 16) | (e4m3fn_code(bf16_hi(w1) / scale) << 24);
+    return code_of<QUANT>(bf16_lo(w0) / scale) | (code_of<QUANT>(bf16_hi(w0) / scale) << 8) |
+           (code_of<QUANT>(bf16_lo(w1) / scale) << 16) | (code_of<QUANT>(bf16_hi(w1) / scale) << 24);
 }
 
 // grid = S; workgroup t quantises x[t]. Lane u owns elements [16u, 16u + 16): two input vectors,
 // one 16-byte output vector of codes. T >= ngroups.
-template <int T>
-__global__ __launch_bounds__(T) void pack_fp8_kernel(
+template <int T, int QUANT>
+__global__ __launch_bounds__(T) void pack_quant_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int ngroups,
     SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
     __shared__ float wave_max[T / 64];
@@ -132,11 +150,11 @@ __global__ __launch_bounds__(T) void pack_fp8_kernel(
 #pragma unroll
     for (int w = 0; w < T / 64; ++w) amax = fmaxf(amax, wave_max[w]);
 
-    const float scale = amax / 448.0f;  // IEEE round-to-nearest division
+    const float scale = amax / code_max<QUANT>();  // IEEE round-to-nearest division
     u32x4 codes = {0u, 0u, 0u, 0u};
     if (u < ngroups && amax > 0.0f)
-        codes = u32x4{quant4(a[0], a[1], scale), quant4(a[2], a[3], scale),
-                      quant4(b[0], b[1], scale), quant4(b[2], b[3], scale)};
+        codes = u32x4{quant4<QUANT>(a[0], a[1], scale), quant4<QUANT>(a[2], a[3], scale),
+                      quant4<QUANT>(b[0], b[1], scale), quant4<QUANT>(b[2], b[3], scale)};
     const uint32_t scale_bits = __float_as_uint(scale);
     const bool tail_lane = u < ((g.tail_end - g.payload_bytes) >> 4);
     const int32_t *slots = slot_idx + (int64_t)t * K;
@@ -147,6 +165,19 @@ __global__ __launch_bounds__(T) void pack_fp8_kernel(
         if (u < ngroups) store16(codes, dst, u << 4);
         if (tail_lane) store_tail(dst, g, u, scale_bits, src_rank, t, k);
     }
+}
+
+template <int QUANT>
+hipError_t launch_quant(const uint8_t *x, const int32_t *slot_idx, int S, int K, int ngroups,
+                        const SlotGeom &g, int src_rank, int64_t max_slots, uint8_t *window,
+                        hipStream_t stream) {
+    if (ngroups <= 512)
+        hipLaunchKernelGGL((pack_quant_kernel<512, QUANT>), dim3(S), dim3(512), 0, stream, x,
+                           slot_idx, K, ngroups, g, src_rank, max_slots, window);
+    else
+        hipLaunchKernelGGL((pack_quant_kernel<1024, QUANT>), dim3(S), dim3(1024), 0, stream, x,
+                           slot_idx, K, ngroups, g, src_rank, max_slots, window);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -165,13 +196,11 @@ hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_
         return hipGetLastError();
     }
     const int ngroups = H / 16;  // 16 elements -> one 16-byte vector of codes
-    if (ngroups <= 512)
-        hipLaunchKernelGGL(pack_fp8_kernel<512>, dim3(S), dim3(512), 0, stream, xb, slot_idx, K,
-                           ngroups, g, src_rank, max_slots, wb);
-    else
-        hipLaunchKernelGGL(pack_fp8_kernel<1024>, dim3(S), dim3(1024), 0, stream, xb, slot_idx, K,
-                           ngroups, g, src_rank, max_slots, wb);
-    return hipGetLastError();
+    if (quant == MOE_QUANT_FP8_E4M3_DYN)
+        return launch_quant<MOE_QUANT_FP8_E4M3_DYN>(xb, slot_idx, S, K, ngroups, g, src_rank,
+                                                    max_slots, wb, stream);
+    return launch_quant<MOE_QUANT_INT8_DYN>(xb, slot_idx, S, K, ngroups, g, src_rank, max_slots,
+                                            wb, stream);
 }
 
 }  // namespace moe

@@ -38,8 +38,9 @@ typedef enum {
 } moe_status;
 
 typedef enum {
-    MOE_QUANT_NONE = 0,        /* bf16 payload                                               */
-    MOE_QUANT_FP8_E4M3_DYN = 1 /* per-token E4M3FN payload + fp32 scale in the slot tail     */
+    MOE_QUANT_NONE = 0,         /* bf16 payload                                              */
+    MOE_QUANT_FP8_E4M3_DYN = 1, /* per-token E4M3FN payload + fp32 scale in the slot tail    */
+    MOE_QUANT_INT8_DYN = 2      /* per-token symmetric INT8 payload + fp32 scale             */
 } moe_quant;
 
 /* Limits. The expert, rank and top-k bounds are those the CAM kernels check ("HCCL Window 模式
@@ -69,7 +70,8 @@ int64_t moe_window_bytes(int32_t S, int32_t K, int32_t H);
  * with scale_off = Ceil(payload_bytes, 32) * 32 and the fp32 scale in its first 4 bytes (zero in
  * bf16 mode); triple int32 (src_rank, token, k) at triple_off = scale_off + 32; zero padding up
  * to tail_end = Ceil(triple_off + 12, 128). moe_dispatch writes exactly [0, tail_end) of each
- * used slot. Any output pointer may be NULL. Returns MOE_OK or a negative moe_status. */
+ * used slot. Both quantised modes have payload_bytes = H. Any output pointer may be NULL. Returns
+ * MOE_OK or a negative moe_status. */
 int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *scale_off,
                      int64_t *triple_off, int64_t *tail_end);
 
@@ -108,11 +110,16 @@ int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t
 
 /* Dispatch pack: for every (t, k) with slot s = slot_idx[t, k] >= 0, write slot s of the window
  * (byte offset s * moe_slot_bytes(H)) as the slot layout above: the bf16 row x[t], or its
- * per-token E4M3FN quantisation (amax over the row, scale = amax / 448 in fp32, codes =
- * E4M3FN(x / scale) rounded to nearest even and saturated; an all-zero row gives scale 0 and zero
- * codes), then the scale block and the triple (src_rank, t, k). This is the CAM InputToShare copy
- * with its DynamicQuant branch ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 and the
- * slot format of section 2.3), with each row read once per token instead of once per copy.
+ * per-token dynamic quantisation with amax = max |x[t]| in fp32:
+ *   MOE_QUANT_FP8_E4M3_DYN: scale = amax / 448, codes = E4M3FN(x / scale), round to nearest even,
+ *                           saturating to +-448;
+ *   MOE_QUANT_INT8_DYN:     scale = amax / 127, codes = clamp(rint(x / scale), -127, 127), rint
+ *                           rounding half to even, two's complement bytes;
+ * every division an IEEE fp32 division; an all-zero row gives scale 0 and zero codes. Then the
+ * scale block and the triple (src_rank, t, k). This is the CAM InputToShare copy with its
+ * DynamicQuant branch ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6, whose quantised output
+ * type is INT8, and the slot format of section 2.3), with each row read once per token instead of
+ * once per copy.
  *
  * In:  x        bf16 [S, H] as raw 16-bit words, 16-byte aligned.
  *      slot_idx int32 [S, K] from moe_layout (or any table of distinct slots); entries < 0 and
@@ -142,6 +149,25 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                 const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
                 int32_t K, void *y, hipStream_t stream);
+
+/* Unpack: window slots -> compact expert input rows ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析",
+ * section 3.9 ShareToOutput, which copies each received slot's token data to the next row of
+ * expandXOut and its triple to expandIdxOut). On one GPU the window is already expert-major with
+ * ascending source tokens, so row s of the output is slot s without its padding and tail: the
+ * contiguous per-expert input of a grouped GEMM, with experts starting at expert_slot_base.
+ *
+ * In:  window      the dispatched window (512-byte aligned, window_bytes >= moe_window_bytes).
+ *      num_slots   DEVICE pointer to N, the number of used slots (e.g. &expert_slot_base[E] from
+ *                  moe_layout); read on the device, so nothing is copied back to the host. Values
+ *                  above S*K are clamped to S*K.
+ *      S, K, H, quant as given to moe_dispatch.
+ * Out: expand_x     [S*K, payload_bytes] bytes, 16-byte aligned: bf16 [., H] or codes [., H].
+ *      expand_scales fp32 [S*K], the per-row scale (quantised modes; may be NULL for bf16).
+ *      expand_idx   int32 [S*K, 3], the (src_rank, token, k) triple of each row.
+ * Rows 0..N-1 are written; rows N..S*K-1 keep their contents. */
+int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,
+               int32_t K, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
+               int32_t *expand_idx, hipStream_t stream);
 
 /* Static description of a moe_status value (never NULL). */
 const char *moe_status_string(int status);

@@ -11,8 +11,8 @@ fp32 reduction), so each function here is the plain definition of its result,
 written out step by step. Citations name the page title and the section on it:
 
 * "HCCL Window 模式 (Non-SHMEM) 代码深度剖析" (the CAM window-mode analysis):
-  section 2.3 (token slot format), 3.6 (InputToShare), 7.8
-  (ReadBufferAndWeightedSum), 8.2 (window size check), 8.3 (core split).
+  section 2.3 (token slot format), 3.6 (InputToShare), 3.9 (ShareToOutput),
+  7.8 (ReadBufferAndWeightedSum), 8.2 (window size check), 8.3 (core split).
 * "Ascend DeepEP MoE Dispatch Optimization": "一条 token 如何走完 MoE" (token path,
   dst_rank), "Dispatch handle 六项分别保存什么" (handle tensors), "Notify 先交换数量和前缀"
   (counts and prefix sums), "Device 侧如何把 channel 变成远端 Put" (per-channel cursor),
@@ -34,10 +34,12 @@ from .layout import channel_bounds, layout, layout_bruteforce
 from .dispatch import (
     slot_geometry,
     quantize_e4m3_dynamic,
+    quantize_int8_dynamic,
     dispatch_slots,
     dispatch_slots_bruteforce,
 )
 from .combine import combine, combine_bruteforce
+from .unpack import unpack
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -50,8 +52,10 @@ __all__ = [
     "layout_bruteforce",
     "slot_geometry",
     "quantize_e4m3_dynamic",
+    "quantize_int8_dynamic",
     "dispatch_slots",
     "dispatch_slots_bruteforce",
     "combine",
     "combine_bruteforce",
+    "unpack",
 ]

@@ -27,12 +27,19 @@ output type. Bytes past the triple are zero up to the 128-byte line end and
 untouched after it; the page leaves their content open.
 
 Dynamic quantisation: the page's DynamicQuant path goes bf16 -> fp32 -> abs ->
-row max -> scale -> narrow, once per token row (section 3.6). The narrow type and
-the scale rule taken here are E4M3FN with scale = amax / 448, the largest E4M3FN
-magnitude, so the row's largest element maps to +-448. Each element is divided
-by the scale in fp32 (IEEE round-to-nearest division) and then narrowed with
-round-to-nearest-even and saturation. A row of zeros gets scale 0 and all-zero
-codes.
+row max -> scale -> narrow, once per token row (section 3.6). Two narrow types:
+
+* E4M3FN with scale = amax / 448, the largest E4M3FN magnitude, so the row's
+  largest element maps to +-448. Each element is divided by the scale in fp32
+  (IEEE round-to-nearest division) and then narrowed with round-to-nearest-even
+  and saturation.
+* INT8, the page's own output type (its tiling key selects an INT8 expandX
+  when DynamicQuant is on). Reading taken for the unstated "Scale" step: the
+  symmetric per-token form scale = amax / 127; each element is divided by the
+  scale in fp32, rounded half to even (the CAST_RINT mode the same page uses)
+  and clamped to [-127, 127]; stored as two's-complement bytes.
+
+In both, a row of zeros gets scale 0 and all-zero codes.
 """
 
 import struct
@@ -44,6 +51,7 @@ from .formats import bf16_bits_to_f32, e4m3fn_encode
 
 QUANT_NONE = 0
 QUANT_FP8_E4M3_DYN = 1
+QUANT_INT8_DYN = 2
 
 SlotGeometry = namedtuple(
     "SlotGeometry", "slot_bytes payload_bytes scale_off triple_off tail_end"
@@ -64,6 +72,23 @@ def slot_geometry(H, quant=QUANT_NONE):
     triple_off = scale_off + 32
     tail_end = min(_ceil(triple_off + 12, 128), slot_bytes)
     return SlotGeometry(slot_bytes, payload, scale_off, triple_off, tail_end)
+
+
+def quantize_int8_dynamic(x_bits):
+    """Per-token dynamic symmetric INT8 quantisation of bf16 rows.
+
+    Returns (codes int8 [S, H], scale float32 [S]). scale = fp32(amax / 127);
+    codes = clamp(rint(fp32(x / scale)), -127, 127) with rint = half to even.
+    """
+    xf = bf16_bits_to_f32(x_bits)
+    amax = np.max(np.abs(xf), axis=1)
+    scale = np.divide(amax, np.float32(127.0), dtype=np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), scale).astype(np.float32)
+    q = np.rint(np.divide(xf, safe[:, None], dtype=np.float32))
+    codes = np.clip(q, -127, 127).astype(np.int8)
+    codes[zero, :] = 0
+    return codes, scale.astype(np.float32)
 
 
 def quantize_e4m3_dynamic(x_bits):
@@ -107,8 +132,9 @@ def dispatch_slots(x_bits, slot_idx, quant=QUANT_NONE, src_rank=0):
     if quant == QUANT_NONE:
         out[s, : 2 * H] = x_bits.view(np.uint8).reshape(S, 2 * H)[t]
     else:
-        codes, scale = quantize_e4m3_dynamic(x_bits)
-        out[s, :H] = codes[t]
+        quantize = quantize_e4m3_dynamic if quant == QUANT_FP8_E4M3_DYN else quantize_int8_dynamic
+        codes, scale = quantize(x_bits)
+        out[s, :H] = codes.view(np.uint8)[t]
         out[s, g.scale_off : g.scale_off + 4] = scale.view(np.uint8).reshape(S, 4)[t]
     triple = np.stack([np.full(n, src_rank), t, k], axis=1).astype("<i4")
     out[s, g.triple_off : g.triple_off + 12] = triple.view(np.uint8).reshape(n, 12)
@@ -132,11 +158,15 @@ def dispatch_slots_bruteforce(x_bits, slot_idx, quant=QUANT_NONE, src_rank=0):
             amax = np.float32(0.0)
             for v in row:
                 amax = max(amax, np.float32(abs(v)))
-            scale = np.float32(np.float32(amax) / np.float32(448.0))
+            top = np.float32(448.0 if quant == QUANT_FP8_E4M3_DYN else 127.0)
+            scale = np.float32(np.float32(amax) / top)
             if amax == 0:
                 codes = bytes(H)
-            else:
+            elif quant == QUANT_FP8_E4M3_DYN:
                 codes = bytes(int(e4m3fn_encode(np.float32(v / scale))) for v in row)
+            else:
+                codes = bytes(int(min(127.0, max(-127.0, float(np.rint(np.float32(v / scale)))))) & 0xFF
+                              for v in row)
             body = codes
             scale_bytes = struct.pack("<f", float(scale))
         for k in range(K):

@@ -89,7 +89,8 @@ def dispatch_call(x=A, slot=A, S=64, H=7168, K=8, quant=0, window=A, nbytes=None
     (dict(S=0), moe.MOE_ERR_ARG),
     (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
     (dict(H=8), moe.MOE_ERR_ARG),
-    (dict(quant=2), moe.MOE_ERR_ARG),
+    (dict(quant=3), moe.MOE_ERR_ARG),
+    (dict(quant=-1), moe.MOE_ERR_ARG),
     (dict(x=A + 8), moe.MOE_ERR_ALIGN),
     (dict(window=A + 256), moe.MOE_ERR_ALIGN),
     (dict(slot=A + 2), moe.MOE_ERR_ALIGN),
@@ -121,6 +122,30 @@ def test_combine_validation(kw, err):
     assert combine_call(**kw) == err
 
 
+def unpack_call(win=A, nbytes=None, num=A, S=64, K=8, H=7168, quant=0, ex=A, sc=A, idx=A):
+    if nbytes is None:
+        nbytes = S * K * 14848
+    return moe._lib.moe_unpack(win, nbytes, num, S, K, H, quant, ex, sc, idx, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(win=NULL), moe.MOE_ERR_ARG),
+    (dict(num=NULL), moe.MOE_ERR_ARG),
+    (dict(ex=NULL), moe.MOE_ERR_ARG),
+    (dict(idx=NULL), moe.MOE_ERR_ARG),
+    (dict(quant=1, sc=NULL), moe.MOE_ERR_ARG),
+    (dict(quant=4), moe.MOE_ERR_ARG),
+    (dict(K=17), moe.MOE_ERR_ARG),
+    (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
+    (dict(win=A + 64), moe.MOE_ERR_ALIGN),
+    (dict(ex=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(num=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(nbytes=64 * 8 * 14848 - 512), moe.MOE_ERR_WINDOW),
+])
+def test_unpack_validation(kw, err):
+    assert unpack_call(**kw) == err
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(moe.moe_status_string(s), str) and moe.moe_status_string(s)
@@ -132,3 +157,4 @@ def test_python_errors_map_to_value_error():
         moe.moe_slot_bytes(1000)
     with pytest.raises(ValueError):
         moe.moe_slot_offsets(7168, 5)
+    assert moe.moe_slot_offsets(7168, moe.MOE_QUANT_INT8_DYN) == moe.moe_slot_offsets(7168, 1)

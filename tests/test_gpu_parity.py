@@ -191,10 +191,26 @@ def test_dispatch_fp8_on_bf16_workload(moe):
                         oracle.slot_geometry(w.H, 1), "fp8 cfg3")
 
 
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_dispatch_int8_workloads(moe, cfg):
+    """INT8 dynamic quant (the pages' own quantised type) on the prefill and outlier rows."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    note(f"dispatch int8 cfg{cfg}")
+    win = gpu_dispatch(moe, inp["x"], slot, 2)
+    assert_window_equal(win, oracle.dispatch_slots(inp["x"], slot, 2, 0),
+                        oracle.slot_geometry(w.H, 2), f"int8 cfg{cfg}")
+
+
 TINY_DISPATCH = [
     # (S, K, H, E, P, quant, seed)
     (1, 1, 16, 1, 1, 0, 1),
     (1, 1, 16, 1, 1, 1, 2),
+    (1, 1, 16, 1, 1, 2, 12),
+    (9, 3, 48, 6, 3, 2, 13),
+    (33, 5, 2064, 10, 5, 2, 14),
+    (6, 16, 16384, 32, 4, 2, 15),
     (9, 3, 48, 6, 3, 1, 3),        # fp8 payload 48 B: 16-byte pad before the scale block
     (33, 5, 2064, 10, 5, 0, 4),    # H not a multiple of the workgroup's vector stride
     (33, 5, 2064, 10, 5, 1, 5),
@@ -226,9 +242,61 @@ def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
     xb = f32_to_bf16_input(np.ones((S, H), np.float32))
-    for quant in (0, 1):
+    for quant in (0, 1, 2):
         win = gpu_dispatch(moe, xb, slot, quant)
         assert np.all(win == POISON)
+
+
+# ---------------------------------------------------------------- unpack
+
+
+def run_unpack(moe, lay_slot, x_bits, S, K, H, E, quant, n_dev):
+    """Dispatch with the given slots, then unpack; outputs poisoned beforehand."""
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(bf16_dev(x_bits), to_dev(lay_slot), win, quant, 7)
+    rows = S * K
+    ex = torch.full((rows, H if quant else 2 * H), POISON, dtype=torch.uint8, device=DEV)
+    sc = torch.full((rows,), -1.0, dtype=torch.float32, device=DEV) if quant else None
+    idx = torch.full((rows, 3), -7, dtype=torch.int32, device=DEV)
+    moe.moe_unpack(win, n_dev, S, K, H, quant, out=(ex, sc, idx))
+    torch.cuda.synchronize()
+    return ex.cpu().numpy(), None if sc is None else sc.cpu().numpy(), idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg,quant", [(3, 0), (4, 1), (4, 2), (5, 0)])
+def test_unpack_workloads(moe, cfg, quant):
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
+    slot = lay.slot_idx.cpu().numpy()
+    note(f"unpack cfg{cfg} quant {quant}")
+    ex, sc, idx = run_unpack(moe, slot, inp["x"], w.S, w.K, w.H, w.E, quant, lay.expert_slot_base[w.E:])
+    rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(inp["x"], slot, quant, 7), w.H, quant)
+    n = rex.shape[0]
+    assert np.array_equal(ex[:n], rex) and np.array_equal(idx[:n], ridx)
+    if quant:
+        assert np.array_equal(sc[:n].view(np.uint32), rsc.view(np.uint32))
+
+
+def test_unpack_partial_and_empty(moe):
+    """N below S*K (masked entries) leaves the rows past N untouched; N = 0 writes nothing."""
+    rng = np.random.default_rng(21)
+    S, K, E, P, H = 50, 4, 12, 4, 2064
+    idx_tab = random_tiny_routing(rng, S, K, E, p_mask=0.4)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    for quant in (0, 1, 2):
+        lay = moe.moe_layout(to_dev(idx_tab), E, P, 3)
+        slot = lay.slot_idx.cpu().numpy()
+        n = int((slot >= 0).sum())
+        ex, sc, idx = run_unpack(moe, slot, xb, S, K, H, E, quant, lay.expert_slot_base[E:])
+        rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(xb, slot, quant, 7), H, quant)
+        assert np.array_equal(ex[:n], rex) and np.array_equal(idx[:n], ridx)
+        assert np.all(ex[n:] == POISON) and np.all(idx[n:] == -7)
+        if quant:
+            assert np.array_equal(sc[:n], rsc) and np.all(sc[n:] == -1.0)
+    zero = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ex, sc, idx = run_unpack(moe, np.full((S, K), -1, np.int32), xb, S, K, H, E, 0, zero)
+    assert np.all(ex == POISON) and np.all(idx == -7)
 
 
 # ---------------------------------------------------------------- combine

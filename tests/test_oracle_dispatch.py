@@ -6,6 +6,8 @@
   back from slot s inverts slot_idx, and every pad byte is zero;
 * fp8 slots: a row quantised by hand, the E4M3 rounding error bound, the amax
   element landing on +-448, a zero row, and the scale as amax/448 to 1 ulp;
+* int8 slots: a row quantised by hand with rounding ties, the half-step error
+  bound, the amax element landing on +-127, a zero row;
 * the vectorised pack equals the one-entry-at-a-time byte-string build.
 """
 
@@ -22,6 +24,7 @@ from oracle import (
     e4m3fn_decode,
     layout,
     quantize_e4m3_dynamic,
+    quantize_int8_dynamic,
     slot_geometry,
 )
 from workloads import WORKLOADS, f32_to_bf16_input, make_inputs, random_tiny_routing
@@ -82,7 +85,7 @@ def test_bf16_payload_and_triple_workload1():
     assert out.shape == (w.S * w.K, slot_geometry(w.H).tail_end)
 
 
-@pytest.mark.parametrize("quant", [0, 1])
+@pytest.mark.parametrize("quant", [0, 1, 2])
 def test_vectorised_equals_bruteforce(quant):
     for seed in range(4):
         x, slot = _tiny_case(seed, H=32 if seed % 2 else 48)
@@ -146,3 +149,41 @@ def test_fp8_quant_error_bound_on_outlier_rows():
     # signs follow x (nonzero codes)
     nz = (codes[live] & 0x7F) != 0
     assert np.all(((codes[live] >> 7) == 1)[nz] == (x[live] < 0)[nz])
+
+
+def test_int8_worked_row():
+    g = read_golden_sections("int8_quant_worked.txt")[""]
+    x = np.array([float(s) for s in g["x"].split()], dtype=np.float32)
+    xb = f32_to_bf16_input(x)[None, :]
+    assert np.array_equal(bf16_bits_to_f32(xb)[0], x)
+    codes, scale = quantize_int8_dynamic(xb)
+    assert scale.view(np.uint32)[0] == int(g["scale_bits"], 16)
+    assert codes[0].view(np.uint8).tolist() == [int(s, 16) for s in g["codes"].split()]
+    geo = slot_geometry(16, 2)
+    reg = dispatch_slots(xb, np.array([[0]], dtype=np.int32), 2, src_rank=1)[0]
+    assert reg[:16].tolist() == codes[0].view(np.uint8).tolist()
+    assert struct.unpack_from("<f", reg.tobytes(), geo.scale_off)[0] == 2.0**-6
+    assert struct.unpack_from("<iii", reg.tobytes(), geo.triple_off) == (1, 0, 0)
+
+
+def test_int8_quant_error_bound():
+    """|q*scale - x| <= scale/2 (plus fp32 division rounding); amax maps to +-127; zero rows."""
+    w = WORKLOADS[4]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    xf = (rng.standard_normal((64, 1024)) * w.x_std).astype(np.float32)
+    xf = np.where(rng.random(xf.shape) < w.outlier_prob, xf * w.outlier_mul, xf).astype(np.float32)
+    xf[5] = 0.0
+    xb = f32_to_bf16_input(xf)
+    codes, scale = quantize_int8_dynamic(xb)
+    x = bf16_bits_to_f32(xb).astype(np.float64)
+    assert scale[5] == 0 and not codes[5].any()
+    live = np.abs(x).max(axis=1) > 0
+    sc = scale[live].astype(np.float64)[:, None]
+    q = codes[live].astype(np.float64)
+    assert np.all(np.abs(q) <= 127)
+    err = np.abs(q * sc - x[live])
+    assert np.all(err <= sc * (0.5 + 127 * 2.0**-23))
+    arg = np.abs(x[live]).argmax(axis=1)
+    top = q[np.arange(live.sum()), arg]
+    assert np.all(np.abs(top) == 127)
+    assert np.all(np.sign(q[q != 0]) == np.sign(x[live][q != 0]))
