@@ -227,7 +227,8 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
-    kernel_key = {"dispatch": "pack_fp8" if w.quant else "pack_bf16", "combine": "combine"}[dom]
+    kernel_key = {"dispatch": {0: "pack_bf16", 1: "pack_fp8", 2: "pack_int8"}[w.quant],
+                  "combine": "combine"}[dom]
     traffic = traffic_from_profiles(f"{kernel_key}:{w.name}")
     roofline = {
         "bound": "hbm", "kernel": kernel_key,
