@@ -7,6 +7,11 @@ whole-step throughput in GB/s of algorithmic bytes, tokens/s, per-kernel event
 timings, the roofline of the dominant kernel and the CPU oracle timed on the
 host cores as a reported baseline.
 
+Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
+at distinct addresses, so each step reads its inputs from HBM rather than from
+the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); extras.warm_same_buffers repeats the timing with
+one set of buffers. extras.copy_ceiling_GB/s is a 1 GiB device-to-device copy.
+
 Algorithmic bytes (what the method must move; zero padding and the window
 reservation are not traffic):
   layout   = topk_idx + is_token_in_rank + counts + slot bases + slot_idx + both prefix matrices
@@ -14,7 +19,8 @@ reservation are not traffic):
   combine  = slot_idx + topk_weights + N * 2H (gathered rows) + y
 with N the number of valid (token, k) entries.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--rotate R]
+       [--quant workload|none|fp8|int8] [--no-extras] [--no-cpu-baseline]
 """
 
 import argparse
@@ -90,6 +96,26 @@ def cpu_baseline(w, C, inp, expert_out, n_valid, min_seconds=10.0, max_reps=25):
     }
 
 
+def copy_ceiling(torch, dev, mib=1024, iters=10):
+    """Device-to-device copy of 1 GiB with torch (read + write bytes per second): the practical
+    bandwidth ceiling next to the 8 TB/s specification."""
+    n = mib * 2**20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
     """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
     payload = 2 * w.H if w.quant == 0 else w.H
@@ -118,8 +144,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--channels", type=int, default=None)
-    ap.add_argument("--rotate", type=int, default=1,
-                    help="independent input sets cycled over the steps (1 = the same batch every step)")
+    ap.add_argument("--rotate", type=int, default=8,
+                    help="input sets cycled over the timed steps, each a copy of the seeded batch at its "
+                         "own addresses, so that no step finds its inputs in the 256 MB memory-side cache "
+                         "(1 = the same buffers every step)")
     ap.add_argument("--quant", choices=["workload", "none", "fp8", "int8"], default="workload",
                     help="dispatch payload type (default: the workload's own)")
     ap.add_argument("--no-extras", action="store_true",
@@ -155,28 +183,17 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    # input sets: set 0 is the seeded workload; further sets (for --rotate) use other seeds of the
-    # same distribution so that a step's inputs are not left in the caches by the previous step
-    sets = [(to_dev(inp["x"]), torch.from_numpy(inp["topk_idx"]).to(dev),
-             torch.from_numpy(inp["topk_weights"]).to(dev), to_dev(eo_host))]
-    for j in range(1, max(1, args.rotate)):
-        wj = dataclasses.replace(w, seed=w.seed + 7919 * j)
-        ij = make_inputs(wj, with_expert_out=False)
-        if int(((ij["topk_idx"] >= 0) & (ij["topk_idx"] < w.E)).sum()) != n_valid:
-            raise RuntimeError("rotated input sets must have the same number of valid entries")
-        sets.append((to_dev(ij["x"]), torch.from_numpy(ij["topk_idx"]).to(dev),
-                     torch.from_numpy(ij["topk_weights"]).to(dev),
-                     to_dev(draw_expert_out(wj.seed + 1000, n_valid, w.H))))
+    # input sets: copies of the seeded batch at distinct addresses. Streaming loads and stores do not
+    # stay in the memory-side cache, but x is read with the default policy, so the copies of x
+    # together must exceed the cache's 256 MB for every timed step to read its inputs from HBM
+    # (cold). Set 0 alone gives the warm case.
+    base = (to_dev(inp["x"]), torch.from_numpy(inp["topk_idx"]).to(dev),
+            torch.from_numpy(inp["topk_weights"]).to(dev), to_dev(eo_host))
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(1, max(1, args.rotate))]
     lay = moe.empty_layout(w.S, w.K, w.E, w.P, C, dev)
     window = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=dev)
     y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        x, topk, wts, eo = sets[i % len(sets)]
-        moe.moe_layout(topk, w.E, w.P, C, out=lay)
-        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
-        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20 // 4
@@ -187,44 +204,52 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def timed(sets_used):
+        """W untimed then K timed steps cycling over sets_used: per-kernel event statistics and the
+        wall time per step between two device synchronisations."""
+        for i in range(args.warmup):
+            x, topk, wts, eo = sets_used[i % len(sets_used)]
+            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            e = ev[i]
+            x, topk, wts, eo = sets_used[i % len(sets_used)]
+            e[0].record(stream)
+            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            e[1].record(stream)
+            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            e[2].record(stream)
+            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = {k: [] for k in ("layout", "dispatch", "combine")}
+        for e in ev:
+            ms["layout"].append(e[0].elapsed_time(e[1]))
+            ms["dispatch"].append(e[1].elapsed_time(e[2]))
+            ms["combine"].append(e[2].elapsed_time(e[3]))
+        kernels = {}
+        for k, v in ms.items():
+            avg_us = 1e3 * float(np.mean(v))
+            gbs = nbytes[k] / (avg_us * 1e-6) / 1e9
+            kernels[k] = {
+                "avg_us": round(avg_us, 2), "min_us": round(1e3 * float(np.min(v)), 2),
+                "median_us": round(1e3 * float(np.median(v)), 2), "bytes": nbytes[k],
+                "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            }
+            if copy_gbs:
+                kernels[k]["frac_copy_ceiling"] = round(gbs / copy_gbs, 4)
+        return kernels, 1e3 * elapsed / args.steps
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        x, topk, wts, eo = sets[i % len(sets)]
-        e[0].record(stream)
-        moe.moe_layout(topk, w.E, w.P, C, out=lay)
-        e[1].record(stream)
-        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
-        e[2].record(stream)
-        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    ms = {k: [] for k in ("layout", "dispatch", "combine")}
-    for e in ev:
-        ms["layout"].append(e[0].elapsed_time(e[1]))
-        ms["dispatch"].append(e[1].elapsed_time(e[2]))
-        ms["combine"].append(e[2].elapsed_time(e[3]))
     nbytes = algorithmic_bytes(w, C, n_valid)
-    kernels = {}
-    for k, v in ms.items():
-        avg_us = 1e3 * float(np.mean(v))
-        gbs = nbytes[k] / (avg_us * 1e-6) / 1e9
-        kernels[k] = {
-            "avg_us": round(avg_us, 2), "min_us": round(1e3 * float(np.min(v)), 2),
-            "median_us": round(1e3 * float(np.median(v)), 2), "bytes": nbytes[k],
-            "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        }
-
+    copy_gbs = None if args.no_extras else copy_ceiling(torch, dev)
+    kernels, ms_per_step = timed(sets)
     total_bytes = sum(nbytes.values())
-    ms_per_step = 1e3 * elapsed / args.steps
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
     kernel_key = {"dispatch": {0: "pack_bf16", 1: "pack_fp8", 2: "pack_int8"}[w.quant],
@@ -260,7 +285,13 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_extras:
-        out["extras"] = {"unpack": time_unpack(moe, torch, w, lay, window, n_valid, stream)}
+        out["extras"] = {"copy_ceiling_GB/s": round(copy_gbs, 1), "copy_method": "torch copy_ (hipMemcpyAsync device to device) of 1 GiB, read+write bytes"}
+        if len(sets) > 1:
+            warm, warm_ms = timed(sets[:1])
+            out["extras"]["warm_same_buffers"] = {
+                "value": round(total_bytes / (warm_ms * 1e-3) / 1e9, 1), "ms_per_step": round(warm_ms, 4),
+                "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
+        out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

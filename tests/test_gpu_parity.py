@@ -398,3 +398,68 @@ def test_python_layer_rejects_bad_window(moe):
     small = torch.empty(moe.moe_window_bytes(4, 2, 64) - 512, dtype=torch.uint8, device=DEV)
     with pytest.raises(ValueError, match="window"):
         moe.moe_dispatch(x, slot, small)
+
+
+# ---------------------------------------------------------------- graph capture
+
+
+def test_step_replays_from_a_captured_graph(moe):
+    """layout -> dispatch -> combine captured once in a HIP graph (the library allocates and
+    synchronises nothing) and replayed on fresh inputs copied into the captured buffers; every
+    replay must equal the eager result on the same inputs. Eager work runs between replays."""
+    w = WORKLOADS[1]
+    S, K, H, E, P, C = w.S, w.K, w.H, w.E, w.P, w.C
+    x_s = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+    idx_s = torch.empty((S, K), dtype=torch.int32, device=DEV)
+    wts_s = torch.empty((S, K), dtype=torch.float32, device=DEV)
+    eo_s = torch.empty((S * K, H), dtype=torch.bfloat16, device=DEV)
+    lay_s = moe.empty_layout(S, K, E, P, C, DEV)
+    win_s = torch.empty(moe.moe_window_bytes(S, K, H), dtype=torch.uint8, device=DEV)
+    y_s = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+
+    def load(seed):
+        rng = np.random.default_rng(seed)
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+        x_s.copy_(bf16_dev(f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))))
+        idx_s.copy_(to_dev(idx))
+        wts_s.copy_(to_dev(rng.random((S, K)).astype(np.float32)))
+        eo_s.copy_(bf16_dev(f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))))
+
+    def step():
+        moe.moe_layout(idx_s, E, P, C, out=lay_s)
+        moe.moe_dispatch(x_s, lay_s.slot_idx, win_s, 0)
+        moe.moe_combine(eo_s, lay_s.slot_idx, wts_s, y=y_s)
+
+    def snapshot():
+        tail = oracle.slot_geometry(H, 0).tail_end
+        return ([t.cpu().numpy().copy() for t in lay_s],
+                win_s.view(S * K, -1)[:, :tail].cpu().numpy().copy(),
+                y_s.view(torch.int16).cpu().numpy().copy())
+
+    load(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        load(seed)
+        torch.cuda.synchronize()
+        step()  # eager reference on the same inputs
+        torch.cuda.synchronize()
+        ref = snapshot()
+        for t in (*lay_s, win_s, y_s):  # poison, then replay
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        note(f"graph replay seed {seed}")
+        for a, b in zip(ref[0], got[0]):
+            assert np.array_equal(a, b)
+        assert np.array_equal(ref[1], got[1]) and np.array_equal(ref[2], got[2])
