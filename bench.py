@@ -11,6 +11,9 @@ Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
 at distinct addresses, so each step reads its inputs from HBM rather than from
 the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); extras.warm_same_buffers repeats the timing with
 one set of buffers. extras.copy_ceiling_GB/s is a 1 GiB device-to-device copy.
+extras.graph_replay times the same step captured in HIP graphs (one per input
+set): the device time per step without Python's launch overhead, which is what
+bounds the event timings at decode sizes.
 
 Algorithmic bytes (what the method must move; zero padding and the window
 reservation are not traffic):
@@ -114,6 +117,41 @@ def copy_ceiling(torch, dev, mib=1024, iters=10):
     gbs = 2 * n * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     return gbs
+
+
+def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
+    """The same step captured once per input set in a HIP graph and replayed: the device time of a
+    step without the Python launch overhead, which dominates at decode sizes."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for x, topk, wts, eo in sets:
+        with torch.cuda.stream(side):  # warm-up on the capture stream
+            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    del graphs
+    return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
@@ -291,6 +329,8 @@ def main():
             out["extras"]["warm_same_buffers"] = {
                 "value": round(total_bytes / (warm_ms * 1e-3) / 1e9, 1), "ms_per_step": round(warm_ms, 4),
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
+        out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
+                                                          total_bytes)
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)

@@ -20,6 +20,9 @@
 //   assign one workgroup per channel: exclusive scan of the per-expert totals (the slot bases), then
 //          slot = base[e] + prefix[e][c-1] + local rank. Workgroup 0 also writes the count vectors.
 // Nothing scans the [S, P] matrix: everything is derived from the K ids of each token.
+// Small tables (decode-sized batches) take the single-launch path in layout_small.hip instead.
+
+#include <stdlib.h>
 
 #include "moe_internal.h"
 
@@ -281,6 +284,12 @@ hipError_t launch_count(const int32_t *topk_idx, int S, int K, int E, int P, int
     return hipGetLastError();
 }
 
+// MOE_LAYOUT_SMALL=0 in the environment turns the single-launch path off (read on every call).
+bool layout_small_enabled() {
+    const char *v = getenv("MOE_LAYOUT_SMALL");
+    return !(v && v[0] == '0');
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
@@ -289,6 +298,10 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
                          int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                          int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                          hipStream_t stream) {
+    if (layout_small_enabled() && layout_small_fits(S, K, E, P, C))
+        return launch_layout_small(topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                                   num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                                   rank_slot_base, expert_slot_base, slot_idx, status, stream);
     hipError_t err;
     if (K <= 1)
         err = launch_count<1>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);

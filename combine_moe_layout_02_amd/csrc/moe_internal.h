@@ -35,6 +35,13 @@ inline SlotGeom slot_geom(int32_t H, int32_t quant) {
     return g;
 }
 
+// Limits of the single-launch layout for small routing tables (its LDS tables are sized by them).
+constexpr int kSmallLayoutEntries = 2048;   // S * K
+constexpr int kSmallLayoutChannels = 1024;  // C
+
+// True when the single-launch layout can take (S, K, E, P, C).
+bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C);
+
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                          int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
@@ -42,6 +49,13 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
                          int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                          int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                          hipStream_t stream);
+
+hipError_t launch_layout_small(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                               int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                               int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                               int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                               int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                               hipStream_t stream);
 
 hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                        int32_t quant, int32_t src_rank, void *window, hipStream_t stream);

@@ -101,7 +101,11 @@ int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *
  *                                          slots are the contiguous range
  *                                          [rank_slot_base[r], rank_slot_base[r+1]).
  *      status                int32 [1]     0, or bit 0 set if an id outside [-1, E) was seen
- * Enqueues three kernels on `stream`. No output may alias an input or another output. */
+ * Enqueues one kernel on `stream` when S*K <= 2048 and C <= 1024 (decode-sized tables: every
+ * workgroup rereads the table and writes its own share of the outputs), otherwise three kernels
+ * (count per channel, scan along channels, assign). Both give identical outputs; setting the
+ * environment variable MOE_LAYOUT_SMALL=0 forces the three-kernel form (read on every call).
+ * No output may alias an input or another output. */
 int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
                uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,

@@ -122,12 +122,26 @@ def assert_bf16_within_ulp(got, ref, what=""):
 # ---------------------------------------------------------------- layout
 
 
+# Small tables go to the single-launch layout unless MOE_LAYOUT_SMALL=0 (read on every call);
+# the tests run both paths on the same inputs.
+LAYOUT_PATHS = ["auto", "three_launch"]
+
+
+@pytest.fixture(params=LAYOUT_PATHS)
+def layout_path(request, monkeypatch):
+    if request.param == "three_launch":
+        monkeypatch.setenv("MOE_LAYOUT_SMALL", "0")
+    else:
+        monkeypatch.delenv("MOE_LAYOUT_SMALL", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("cfg", sorted(WORKLOADS))
-def test_layout_workloads(moe, cfg):
+def test_layout_workloads(moe, cfg, layout_path):
     w = WORKLOADS[cfg]
     idx = inputs(cfg)["topk_idx"]
     for C in sorted({w.C, 1, 3, min(w.S, 4096)}):
-        note(f"layout cfg{cfg} {w.describe()} C={C}")
+        note(f"layout cfg{cfg} {w.describe()} C={C} path={layout_path}")
         assert_layout_equal(gpu_layout(moe, idx, w.E, w.P, C), oracle.layout(idx, w.E, w.P, C),
                             f"cfg{cfg} C={C}")
 
@@ -141,28 +155,35 @@ TINY_LAYOUTS = [
     (257, 2, 384, 384, 257, 0.0, 0.0, 5),  # P_MAX, one expert per rank, C = S
     (1000, 8, 64, 8, 1, 0.05, 0.0, 6),    # one channel, many chunks
     (600, 6, 5, 5, 600, 0.5, 0.02, 7),    # heavy masking, duplicate-prone
+    (256, 8, 256, 8, 128, 0.0, 0.0, 8),   # S*K = 2048: largest table of the single-launch path
+    (257, 8, 256, 8, 128, 0.0, 0.0, 9),   # one token more: three launches
+    (64, 8, 512, 256, 64, 0.1, 0.05, 10),  # E at its maximum on the single-launch path
+    (64, 4, 384, 384, 64, 0.1, 0.0, 12),  # P at its maximum on the single-launch path
+    (2048, 1, 16, 4, 1024, 0.1, 0.0, 13),  # S*K = 2048 with K = 1, C at its maximum (1024)
+    (200, 3, 9, 3, 7, 0.0, 0.0, 11),      # S not a multiple of 64, ragged channels
 ]
 
 
 @pytest.mark.parametrize("case", TINY_LAYOUTS)
-def test_layout_tiny_adversarial(moe, case):
+def test_layout_tiny_adversarial(moe, case, layout_path):
     S, K, E, P, C, p_mask, p_bad, seed = case
     rng = np.random.default_rng(seed)
     idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
-    note(f"layout tiny {case}")
+    note(f"layout tiny {case} path={layout_path}")
     assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), str(case))
 
 
-def test_layout_special_tables(moe):
+def test_layout_special_tables(moe, layout_path):
     S, K, E, P = 96, 4, 16, 4
     cases = {
         "all_masked": np.full((S, K), -1, np.int32),
         "one_expert": np.full((S, K), 5, np.int32),  # every entry to expert 5, duplicates in rows
         "empty_experts": np.tile(np.array([0, 1, 14, 15], np.int32), (S, 1)),
+        "all_bad": np.full((S, K), E + 3, np.int32),
     }
     for name, idx in cases.items():
         for C in (1, 3, S):
-            note(f"layout special {name} C={C}")
+            note(f"layout special {name} C={C} path={layout_path}")
             assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), name)
 
 
