@@ -16,8 +16,10 @@ written out step by step. Citations name the page title and the section on it:
 * "Ascend DeepEP MoE Dispatch Optimization": "一条 token 如何走完 MoE" (token path,
   dst_rank), "Dispatch handle 六项分别保存什么" (handle tensors), "Notify 先交换数量和前缀"
   (counts and prefix sums), "Device 侧如何把 channel 变成远端 Put" (per-channel cursor),
-  "所谓 compact plan 到底压缩了什么" (compact destination plan).
-* "internode.cu", section 1 notify_dispatch (per-rank / per-expert counting).
+  "所谓 compact plan 到底压缩了什么" (compact destination plan), "输出长度有动态和固定两种模式"
+  (fixed-length num_worst_tokens outputs).
+* "internode.cu", section 1 notify_dispatch (per-rank / per-expert counting, the
+  expert_alignment rounding of the per-expert counts).
 
 Where the pages leave a step open, the reading taken is stated in the function's
 docstring.
@@ -39,7 +41,7 @@ from .dispatch import (
     dispatch_slots_bruteforce,
 )
 from .combine import combine, combine_bruteforce
-from .unpack import unpack
+from .unpack import aligned_row_base, unpack, unpack_padded
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -58,4 +60,6 @@ __all__ = [
     "combine",
     "combine_bruteforce",
     "unpack",
+    "aligned_row_base",
+    "unpack_padded",
 ]

@@ -53,3 +53,77 @@ def test_unpack_quantised_rows_and_scales(quant):
         codes, _ = quantize_int8_dynamic(xb)
         for t, k in zip(*np.nonzero(slot >= 0)):
             assert np.array_equal(ex[slot[t, k]].view(np.int8), codes[t])
+
+
+# ---------------------------------------------------------------- padded unpack
+
+from oracle import aligned_row_base, slot_geometry, unpack_padded  # noqa: E402
+
+
+def _labelled_regions(n, H, quant):
+    """n slots whose payload bytes, scale and triple all identify the slot (no pack involved)."""
+    g = slot_geometry(H, quant)
+    reg = np.zeros((n, g.tail_end), dtype=np.uint8)
+    for s in range(n):
+        reg[s, : g.payload_bytes] = (s * 37 + np.arange(g.payload_bytes)) % 251 + 1
+        reg[s, g.triple_off : g.triple_off + 12] = np.array([5, s, 100 + s], "<i4").view(np.uint8)
+        if quant:
+            reg[s, g.scale_off : g.scale_off + 4] = np.array([0.5 + s], "<f4").view(np.uint8)
+    return reg
+
+
+@pytest.mark.parametrize("quant", [0, 1])
+def test_unpack_padded_worked_examples(golden, quant):
+    esb = [0, 2, 2, 3, 4, 4, 4, 5, 7]
+    H = 32
+    reg = _labelled_regions(7, H, quant)
+    g = slot_geometry(H, quant)
+    for name, sec in golden("unpack_padded_worked.txt").items():
+        if not name:
+            continue
+        A, R = (int(v) for v in sec["A R"].split())
+        ex, idx, sc, base, trunc = unpack_padded(reg, esb, H, quant, A, R)
+        assert base.tolist() == [int(v) for v in sec["row_base"].split()], name
+        assert aligned_row_base(esb, A).tolist() == base.tolist()
+        assert trunc == bool(int(sec["truncated"])), name
+        src = [int(v) for v in sec["row_source"].split()]
+        assert ex.shape == (R, g.payload_bytes) and idx.shape == (R, 3) and len(src) == R
+        for row, s in enumerate(src):
+            if s < 0:
+                assert not ex[row].any() and idx[row].tolist() == [-1, -1, -1], (name, row)
+                if quant:
+                    assert sc[row] == 0.0
+            else:
+                assert np.array_equal(ex[row], reg[s, : g.payload_bytes]), (name, row)
+                assert idx[row].tolist() == [5, s, 100 + s], (name, row)
+                if quant:
+                    assert sc[row] == np.float32(0.5 + s)
+        if not quant:
+            assert sc is None
+
+
+def test_unpack_padded_invariants_on_random_layouts():
+    """Every slot lands exactly once, in order, at an aligned block start + its index; each
+    expert's block is a multiple of the alignment; padding rows are zero / -1."""
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        S, K, E, P = int(rng.integers(1, 40)), int(rng.integers(1, 5)), 8, 4
+        tab = random_tiny_routing(rng, S, K, E, p_mask=0.2)
+        esb = layout(tab, E, P, 1)["expert_slot_base"]
+        n = int(esb[-1])
+        A = int(rng.integers(1, 9))
+        base = aligned_row_base(esb, A)
+        assert np.all(np.diff(base) % A == 0) and np.all(np.diff(base) >= np.diff(esb))
+        assert np.all(np.diff(base) - np.diff(esb) < A)  # less than one block of padding each
+        R = int(base[-1]) + int(rng.integers(-3, 4))
+        if R < 1:
+            continue
+        reg = _labelled_regions(max(n, 1), 16, 0)[:n]
+        ex, idx, _, b2, trunc = unpack_padded(reg, esb, 16, 0, A, R)
+        assert trunc == (base[-1] > R)
+        seen = idx[idx[:, 0] >= 0, 1]
+        assert np.array_equal(seen, np.arange(len(seen)))  # slots in order, none twice
+        assert len(seen) == min(n, sum(max(0, min(int(esb[e + 1] - esb[e]), R - int(base[e])))
+                                       for e in range(E)))
+        pad = idx[:, 0] < 0
+        assert not ex[pad].any() and np.all(idx[pad] == -1)
