@@ -154,6 +154,29 @@ def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes)
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
+def time_unpack_padded(moe, torch, w, lay, window, n_valid, stream, A=16, iters=20):
+    """moe_unpack_padded of the last dispatched window with expert_alignment A into the worst-case
+    row count S*K + E*(A-1), which needs no count read back (outside the timed step)."""
+    R = w.S * w.K + w.E * (A - 1)
+    payload = 2 * w.H if w.quant == 0 else w.H
+    out = None
+    ms = []
+    for i in range(iters + 3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = moe.moe_unpack_padded(window, lay.expert_slot_base, w.S, w.K, w.H, w.quant, A, R, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    per_row = payload + 12 + (4 if w.quant else 0)
+    nbytes = n_valid * per_row + R * per_row + 8 * (w.E + 1) + 4
+    avg_us = 1e3 * float(np.mean(ms))
+    return {"alignment": A, "rows": R, "avg_us": round(avg_us, 2), "bytes": nbytes,
+            "GB/s": round(nbytes / avg_us / 1e3, 1), "frac_hbm_peak": round(nbytes / avg_us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
     """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
     payload = 2 * w.H if w.quant == 0 else w.H
@@ -332,6 +355,7 @@ def main():
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                           total_bytes)
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
+        out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

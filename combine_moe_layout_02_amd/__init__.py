@@ -30,7 +30,7 @@ MOE_QUANT_INT8_DYN = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
-    "moe_combine", "moe_unpack", "moe_status_string",
+    "moe_combine", "moe_unpack", "moe_unpack_padded", "moe_status_string",
 )
 
 
@@ -54,6 +54,8 @@ def _load():
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
         "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
+        "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
+                                             P, P, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -260,9 +262,60 @@ def moe_unpack(window, num_slots, S, K, H, quant=MOE_QUANT_NONE, out=None, strea
     return out
 
 
+class PaddedUnpacked(NamedTuple):
+    expand_x: torch.Tensor  # [R, H] bf16, or uint8 codes for the quantised modes
+    expand_scales: torch.Tensor  # fp32 [R] (quantised modes) or None
+    expand_idx: torch.Tensor  # int32 [R, 3], (-1, -1, -1) on padding rows
+    expert_row_base: torch.Tensor  # int32 [E + 1], aligned first row of each expert
+    status: torch.Tensor  # int32 [1], 1 if the aligned rows exceeded R
+
+
+def moe_unpack_padded(window, expert_slot_base, S, K, H, quant=MOE_QUANT_NONE, expert_alignment=1,
+                      out_rows=None, out=None, stream=None):
+    """Unpack into exactly out_rows rows (default S*K) with each expert's block starting at a
+    multiple of expert_alignment; padding rows are zero with triple -1. expert_slot_base is the
+    layout's device tensor [E + 1]; nothing is read back to the host."""
+    _need(window, "window")
+    dev = window.device
+    _need(expert_slot_base, "expert_slot_base", torch.int32, 1, dev)
+    S, K, H, quant = int(S), int(K), int(H), int(quant)
+    E = expert_slot_base.shape[0] - 1
+    R = S * K if out_rows is None else int(out_rows)
+    if out is None:
+        if quant == MOE_QUANT_NONE:
+            ex = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            sc = None
+        else:
+            ex = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty(R, dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = PaddedUnpacked(ex, sc, torch.empty((R, 3), **i32), torch.empty(E + 1, **i32),
+                             torch.empty(1, **i32))
+    ex, sc, idx, base, status = out
+    _need(ex, "expand_x", device=dev)
+    _need(idx, "expand_idx", torch.int32, 2, dev)
+    _need(base, "expert_row_base", torch.int32, 1, dev)
+    _need(status, "status", torch.int32, device=dev)
+    payload = moe_slot_offsets(H, quant)["payload_bytes"]
+    if ex.numel() * ex.element_size() < R * payload or tuple(idx.shape) != (R, 3):
+        raise ValueError("expand_x must hold out_rows rows of payload bytes and expand_idx [out_rows, 3]")
+    if base.shape[0] != E + 1 or status.numel() < 1:
+        raise ValueError("expert_row_base must have E + 1 entries and status one")
+    if sc is not None:
+        _need(sc, "expand_scales", torch.float32, device=dev)
+        if sc.numel() < R:
+            raise ValueError("expand_scales must hold out_rows values")
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_unpack_padded(_ptr(window), nbytes, _ptr(expert_slot_base), E, S, K, H, quant,
+                                  int(expert_alignment), R, _ptr(ex), None if sc is None else _ptr(sc),
+                                  _ptr(idx), _ptr(base), _ptr(status), _stream(dev, stream)))
+    return out
+
+
 __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_combine", "moe_unpack", "Unpacked", "moe_status_string",
+    "moe_dispatch", "moe_combine", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_status_string",
 ]

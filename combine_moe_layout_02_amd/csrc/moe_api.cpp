@@ -131,6 +131,32 @@ int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slot
                                        expand_idx, stream));
 }
 
+int moe_unpack_padded(const void *window, int64_t window_bytes, const int32_t *expert_slot_base,
+                      int32_t E, int32_t S, int32_t K, int32_t H, int32_t quant,
+                      int32_t expert_alignment, int64_t out_rows, void *expand_x,
+                      float *expand_scales, int32_t *expand_idx, int32_t *expert_row_base,
+                      int32_t *status, hipStream_t stream) {
+    if (!window || !expert_slot_base || !expand_x || !expand_idx || !expert_row_base || !status)
+        return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    if (quant != MOE_QUANT_NONE && !expand_scales) return MOE_ERR_ARG;
+    if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_ARG;
+    if (expert_alignment < 1 || expert_alignment > MOE_MAX_ALIGNMENT) return MOE_ERR_ARG;
+    if (out_rows < 1 || out_rows > MOE_MAX_OUT_ROWS) return MOE_ERR_ARG;
+    if (!aligned(window, 512) || !aligned(expand_x, 16) || !aligned(expert_slot_base, 4) ||
+        !aligned(expand_idx, 4) || !aligned(expert_row_base, 4) || !aligned(status, 4) ||
+        (expand_scales && !aligned(expand_scales, 4)))
+        return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_unpack_padded(window, expert_slot_base, E, S, K, H, quant,
+                                              expert_alignment, out_rows, expand_x, expand_scales,
+                                              expand_idx, expert_row_base, status, stream));
+}
+
 const char *moe_status_string(int status) {
     switch (status) {
         case MOE_OK: return "ok";

@@ -64,6 +64,12 @@ hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int6
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,
                           int32_t H, int32_t K, void *y, hipStream_t stream);
 
+hipError_t launch_unpack_padded(const void *window, const int32_t *expert_slot_base, int32_t E,
+                                int32_t S, int32_t K, int32_t H, int32_t quant,
+                                int32_t expert_alignment, int64_t out_rows, void *expand_x,
+                                float *expand_scales, int32_t *expand_idx,
+                                int32_t *expert_row_base, int32_t *status, hipStream_t stream);
+
 hipError_t launch_unpack(const void *window, const int32_t *num_slots, int32_t S, int32_t K,
                          int32_t H, int32_t quant, void *expand_x, float *expand_scales,
                          int32_t *expand_idx, hipStream_t stream);

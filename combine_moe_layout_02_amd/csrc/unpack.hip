@@ -1,4 +1,5 @@
-// Unpack kernel for gfx950: window slots -> compact expert input rows, triples and scales.
+// Unpack kernels for gfx950: window slots -> compact expert input rows, triples and scales, and a
+// padded form with expert_alignment-rounded row blocks and a fixed number of output rows.
 //
 // The CAM receive side ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.9 ShareToOutput)
 // copies every received slot's token data to the next row of expandXOut and its triple to
@@ -8,8 +9,17 @@
 //
 // The number of used slots N is read on the device (for example expert_slot_base[E] written by the
 // layout), so no count is read back to the host; the grid covers the worst case S*K and workgroups
-// past N exit at once. Like the bf16 pack, each workgroup owns one (slot, part) of kPartThreads
-// 16-byte vectors: one non-temporal load (the slot is read once) and one streaming store per lane.
+// past N exit at once. Each workgroup owns one (slot, part) of kPartThreads 16-byte vectors: one
+// non-temporal load (the slot is read once) and one streaming store per lane. One-wave parts were
+// fastest on MI355X at H=7168 (bf16: 146 us against 148 us for 128 lanes; fp8 codes, whose 448
+// vectors split evenly into 64-lane parts but not 128-lane ones: 76 us against 94 us).
+//
+// The padded form follows two options of DeepEP's normal dispatch: expert_alignment, which rounds
+// every per-expert row count up to a multiple of the alignment ("internode.cu", section 1
+// notify_dispatch), and num_worst_tokens, a fixed output length that needs no count read back on
+// the host, with zero data and -1 indices in the rows past the real ones ("Ascend DeepEP MoE
+// Dispatch Optimization", section "输出长度有动态和固定两种模式"). Expert e's rows start at the
+// aligned offset row_base[e], so every expert's block of a grouped GEMM starts on a tile boundary.
 
 #include "moe_internal.h"
 
@@ -18,7 +28,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPartThreads = 128;
+constexpr int kPartThreads = 64;
 constexpr int kLoadPolicy = 2;             // nt
 constexpr int kStorePolicy = 1 | 16 | 2;   // sc0 sc1 nt
 
@@ -59,7 +69,119 @@ __global__ __launch_bounds__(kPartThreads) void unpack_kernel(
     }
 }
 
+constexpr int kBaseThreads = 512;  // >= MOE_MAX_EXPERTS: one expert per lane
+
+// row_base[e] = sum over e' < e of ceil(count[e'] / A) * A with count[e] = esb[e+1] - esb[e]
+// (the expert_alignment rounding of "internode.cu", section 1 notify_dispatch); row_base[E] is the
+// aligned total, and status = 1 when it exceeds the out_rows rows of the output.
+__global__ __launch_bounds__(kBaseThreads) void unpack_row_base_kernel(
+    const int32_t *__restrict__ esb, int E, int A, int64_t out_rows, int32_t *__restrict__ row_base,
+    int32_t *__restrict__ status) {
+    __shared__ int32_t wave_sum[kBaseThreads / 64];
+    const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+    int n = 0;
+    if (e < E) {
+        const int cnt = max(esb[e + 1] - esb[e], 0);
+        n = (cnt + A - 1) / A * A;
+    }
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += u;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kBaseThreads / 64; ++w) {
+        before += w < wave ? wave_sum[w] : 0;
+        total += wave_sum[w];
+    }
+    if (e < E) row_base[e] = before + incl - n;
+    if (e == 0) {
+        row_base[E] = total;
+        *status = (int64_t)total > out_rows ? 1 : 0;
+    }
+}
+
+// grid = out_rows * nparts; workgroup (r, q) writes vectors [q*kPartThreads, (q+1)*kPartThreads)
+// of output row r: the part of its source slot's payload, or zeros for a padding row. Lane 0 of
+// the last part writes the triple and the scale (-1s and 0 for padding). The row's expert is
+// found by a binary search over row_base (E + 1 values, uniform per workgroup).
+__global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
+    const uint8_t *__restrict__ window, const int32_t *__restrict__ esb,
+    const int32_t *__restrict__ row_base, int E, int64_t max_slots, int nparts, SlotGeom g,
+    bool quantised, uint8_t *__restrict__ expand_x, float *__restrict__ expand_scales,
+    int32_t *__restrict__ expand_idx) {
+    const int64_t r = blockIdx.x / nparts;
+    const int q = blockIdx.x - (int)(r * nparts);
+    const int lane = threadIdx.x;
+    const int v = q * kPartThreads + lane;
+    int64_t s = -1;
+    if (r < row_base[E]) {
+        int lo = 0, hi = E;  // largest e with row_base[e] <= r
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (row_base[mid] <= r) lo = mid;
+            else hi = mid;
+        }
+        const int64_t j = r - row_base[lo];
+        if (j < (int64_t)esb[lo + 1] - esb[lo]) s = esb[lo] + j;
+        if (s >= max_slots) s = -1;  // a corrupt base table never reads past the window
+    }
+    const bool in_row = (v << 4) < g.payload_bytes;
+    u32x4 d = {0u, 0u, 0u, 0u};
+    __amdgpu_buffer_rsrc_t src = rsrc(window, 0);
+    if (s >= 0) {
+        src = rsrc(window + s * g.slot_bytes, g.tail_end);
+        if (in_row) d = __builtin_amdgcn_raw_buffer_load_b128(src, v << 4, 0, kLoadPolicy);
+    }
+    if (in_row) {
+        const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + r * g.payload_bytes, g.payload_bytes);
+        __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
+    }
+    if (q == nparts - 1 && lane == 0) {
+        int32_t *idx = expand_idx + r * 3;
+        float scale = 0.0f;
+        if (s >= 0) {
+            const u32x4 tr = __builtin_amdgcn_raw_buffer_load_b128(src, g.triple_off, 0, kLoadPolicy);
+            idx[0] = (int32_t)tr.x;
+            idx[1] = (int32_t)tr.y;
+            idx[2] = (int32_t)tr.z;
+            if (quantised)
+                scale = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(src, g.scale_off, 0, kLoadPolicy));
+        } else {
+            idx[0] = -1;
+            idx[1] = -1;
+            idx[2] = -1;
+        }
+        if (quantised) expand_scales[r] = scale;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_unpack_padded(const void *window, const int32_t *expert_slot_base, int32_t E,
+                                int32_t S, int32_t K, int32_t H, int32_t quant,
+                                int32_t expert_alignment, int64_t out_rows, void *expand_x,
+                                float *expand_scales, int32_t *expand_idx,
+                                int32_t *expert_row_base, int32_t *status, hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, quant);
+    hipLaunchKernelGGL(unpack_row_base_kernel, dim3(1), dim3(kBaseThreads), 0, stream,
+                       expert_slot_base, E, expert_alignment, out_rows, expert_row_base, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nvec = g.payload_bytes / 16;
+    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+    hipLaunchKernelGGL(unpack_padded_kernel, dim3((uint32_t)(out_rows * nparts)),
+                       dim3(kPartThreads), 0, stream, static_cast<const uint8_t *>(window),
+                       expert_slot_base, expert_row_base, E, (int64_t)S * K, nparts, g,
+                       quant != MOE_QUANT_NONE, static_cast<uint8_t *>(expand_x), expand_scales,
+                       expand_idx);
+    return hipGetLastError();
+}
 
 hipError_t launch_unpack(const void *window, const int32_t *num_slots, int32_t S, int32_t K,
                          int32_t H, int32_t quant, void *expand_x, float *expand_scales,

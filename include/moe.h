@@ -52,6 +52,8 @@ typedef enum {
 #define MOE_MAX_CHANNELS 4096
 #define MOE_MAX_TOKENS 65536
 #define MOE_MAX_HIDDEN 16384
+#define MOE_MAX_ALIGNMENT 65536   /* expert_alignment of moe_unpack_padded */
+#define MOE_MAX_OUT_ROWS 1048576  /* out_rows of moe_unpack_padded */
 
 /* Bytes of one window slot: Ceil(Ceil(2H, 32) * 32 + 44, 512) * 512, the dispatch token size of
  * "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 8.2 (Window 大小校验): the bf16 row padded to
@@ -172,6 +174,39 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
 int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,
                int32_t K, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
                int32_t *expand_idx, hipStream_t stream);
+
+/* Padded unpack: the rows of moe_unpack placed for a grouped GEMM whose per-expert blocks start on
+ * a multiple of expert_alignment, in an output of exactly out_rows rows. Two options of DeepEP's
+ * normal dispatch: expert_alignment rounds every per-expert row count up to a multiple of the
+ * alignment ("internode.cu", section 1 notify_dispatch), and num_worst_tokens fixes the output
+ * length so that no count has to be read back on the host, with zero data and -1 indices in the
+ * rows past the real ones ("Ascend DeepEP MoE Dispatch Optimization", section
+ * "输出长度有动态和固定两种模式").
+ *
+ *   count[e]    = expert_slot_base[e+1] - expert_slot_base[e]
+ *   row_base[e] = sum over e' < e of ceil(count[e'] / A) * A,   row_base[E] = the aligned total
+ *   row row_base[e] + j (j < count[e]) <- slot expert_slot_base[e] + j, as moe_unpack writes it;
+ *   every other row r < out_rows is padding: zero bytes, scale 0, triple (-1, -1, -1).
+ *
+ * In:  window, window_bytes, S, K, H, quant as for moe_unpack.
+ *      expert_slot_base  DEVICE int32 [E+1] from moe_layout; read on the device.
+ *      E                 in [1, MOE_MAX_EXPERTS].
+ *      expert_alignment  A in [1, MOE_MAX_ALIGNMENT].
+ *      out_rows          R in [1, MOE_MAX_OUT_ROWS].
+ * Out (all R rows fully written):
+ *      expand_x          [R, payload_bytes] bytes, 16-byte aligned.
+ *      expand_scales     fp32 [R] (quantised modes; may be NULL for bf16).
+ *      expand_idx        int32 [R, 3].
+ *      expert_row_base   int32 [E+1], row_base above (the grouped GEMM's group offsets; the
+ *                        aligned count of expert e is row_base[e+1] - row_base[e]).
+ *      status            int32 [1]: 1 if row_base[E] > R (rows at or past R were dropped; the page
+ *                        notes the same truncation happens silently in DeepEP), else 0.
+ * Enqueues two kernels on `stream`; nothing is read back to the host. */
+int moe_unpack_padded(const void *window, int64_t window_bytes, const int32_t *expert_slot_base,
+                      int32_t E, int32_t S, int32_t K, int32_t H, int32_t quant,
+                      int32_t expert_alignment, int64_t out_rows, void *expand_x,
+                      float *expand_scales, int32_t *expand_idx, int32_t *expert_row_base,
+                      int32_t *status, hipStream_t stream);
 
 /* Static description of a moe_status value (never NULL). */
 const char *moe_status_string(int status);

@@ -158,3 +158,33 @@ def test_python_errors_map_to_value_error():
     with pytest.raises(ValueError):
         moe.moe_slot_offsets(7168, 5)
     assert moe.moe_slot_offsets(7168, moe.MOE_QUANT_INT8_DYN) == moe.moe_slot_offsets(7168, 1)
+
+
+def unpack_padded_call(win=A, nbytes=None, esb=A, E=256, S=64, K=8, H=7168, quant=0, align=16,
+                       rows=1024, ex=A, sc=A, idx=A, base=A, st=A):
+    if nbytes is None:
+        nbytes = S * K * 14848
+    return moe._lib.moe_unpack_padded(win, nbytes, esb, E, S, K, H, quant, align, rows, ex, sc, idx,
+                                      base, st, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(win=NULL), moe.MOE_ERR_ARG),
+    (dict(esb=NULL), moe.MOE_ERR_ARG),
+    (dict(base=NULL), moe.MOE_ERR_ARG),
+    (dict(st=NULL), moe.MOE_ERR_ARG),
+    (dict(quant=2, sc=NULL), moe.MOE_ERR_ARG),
+    (dict(E=0), moe.MOE_ERR_ARG),
+    (dict(E=513), moe.MOE_ERR_ARG),
+    (dict(align=0), moe.MOE_ERR_ARG),
+    (dict(align=65537), moe.MOE_ERR_ARG),
+    (dict(rows=0), moe.MOE_ERR_ARG),
+    (dict(rows=1048577), moe.MOE_ERR_ARG),
+    (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
+    (dict(ex=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(esb=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(st=A + 1), moe.MOE_ERR_ALIGN),
+    (dict(nbytes=64 * 8 * 14848 - 512), moe.MOE_ERR_WINDOW),
+])
+def test_unpack_padded_validation(kw, err):
+    assert unpack_padded_call(**kw) == err

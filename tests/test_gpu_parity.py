@@ -320,6 +320,73 @@ def test_unpack_partial_and_empty(moe):
     assert np.all(ex == POISON) and np.all(idx == -7)
 
 
+def run_unpack_padded(moe, lay, x_bits, S, K, H, E, quant, A, R):
+    """Dispatch with the layout's slots, then the padded unpack into poisoned outputs."""
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(bf16_dev(x_bits), lay.slot_idx, win, quant, 3)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    out = moe.PaddedUnpacked(
+        torch.full((R, H if quant else 2 * H), POISON, dtype=torch.uint8, device=DEV),
+        torch.full((R,), -1.0, dtype=torch.float32, device=DEV) if quant else None,
+        torch.full((R, 3), -7, **i32), torch.full((E + 1,), -7, **i32), torch.full((1,), -7, **i32))
+    moe.moe_unpack_padded(win, lay.expert_slot_base, S, K, H, quant, A, R, out=out)
+    torch.cuda.synchronize()
+    return [None if t is None else t.cpu().numpy() for t in out]
+
+
+def assert_padded_equal(got, ref, what):
+    ex, sc, idx, base, status = got
+    rex, ridx, rsc, rbase, rtrunc = ref
+    assert np.array_equal(base, rbase), what
+    assert int(status[0]) == int(rtrunc), what
+    assert np.array_equal(idx, ridx), what
+    assert np.array_equal(ex, rex), what
+    if rsc is not None:
+        assert np.array_equal(sc.view(np.uint32), rsc.view(np.uint32)), what
+
+
+@pytest.mark.parametrize("cfg,quant", [(1, 0), (2, 1), (3, 0), (4, 2)])
+def test_unpack_padded_workloads(moe, cfg, quant):
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
+    slot = lay.slot_idx.cpu().numpy()
+    esb = lay.expert_slot_base.cpu().numpy()
+    regions = oracle.dispatch_slots(inp["x"], slot, quant, 3)
+    # (alignment, rows relative to the aligned total): exact fit, extra padding rows, truncation
+    cases = [(1, 0), (16, 37), (128, -1000)] if w.S * w.K > 4096 else \
+        [(a, d) for a in (1, 16, 128) for d in (0, 37, -1000)]
+    for A, d in cases:
+        total = int(oracle.aligned_row_base(esb, A)[-1])
+        R = max(1, total + d)
+        note(f"unpack_padded cfg{cfg} quant {quant} A={A} R={R} (aligned total {total})")
+        got = run_unpack_padded(moe, lay, inp["x"], w.S, w.K, w.H, w.E, quant, A, R)
+        ref = oracle.unpack_padded(regions, esb, w.H, quant, A, R)
+        assert_padded_equal(got, ref, f"cfg{cfg} A={A} R={R}")
+
+
+def test_unpack_padded_tiny_and_degenerate(moe):
+    """Masked entries, empty experts, R = 1, alignment larger than every count."""
+    rng = np.random.default_rng(33)
+    S, K, E, P, H = 40, 3, 12, 4, 48
+    tab = random_tiny_routing(rng, S, K, E, p_mask=0.3)
+    tab[:, :] = np.where(np.isin(tab, [2, 3]), -1, tab)  # experts 2 and 3 receive nothing
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    lay = moe.moe_layout(to_dev(tab), E, P, 3)
+    slot = lay.slot_idx.cpu().numpy()
+    esb = lay.expert_slot_base.cpu().numpy()
+    for quant in (0, 1):
+        regions = oracle.dispatch_slots(xb, slot, quant, 3)
+        for A, R in ((1, 1), (5, 64), (64, 1000), (7, int(esb[-1])), (3, 17)):
+            note(f"unpack_padded tiny quant {quant} A={A} R={R}")
+            got = run_unpack_padded(moe, lay, xb, S, K, H, E, quant, A, R)
+            ref = oracle.unpack_padded(regions, esb, H, quant, A, R)
+            assert_padded_equal(got, ref, f"tiny quant {quant} A={A} R={R}")
+    empty = moe.moe_layout(to_dev(np.full((S, K), -1, np.int32)), E, P, 3)
+    got = run_unpack_padded(moe, empty, xb, S, K, H, E, 0, 8, 20)
+    assert np.all(got[2] == -1) and not got[0].any() and np.all(got[3] == 0) and got[4][0] == 0
+
+
 # ---------------------------------------------------------------- combine
 
 
