@@ -40,7 +40,7 @@ from .dispatch import (
     dispatch_slots,
     dispatch_slots_bruteforce,
 )
-from .combine import combine, combine_bruteforce
+from .combine import combine, combine_bruteforce, combine_scatter, combine_staged
 from .unpack import aligned_row_base, unpack, unpack_padded
 
 __all__ = [
@@ -59,6 +59,8 @@ __all__ = [
     "dispatch_slots_bruteforce",
     "combine",
     "combine_bruteforce",
+    "combine_scatter",
+    "combine_staged",
     "unpack",
     "aligned_row_base",
     "unpack_padded",

@@ -56,3 +56,33 @@ def combine_bruteforce(expert_out_bits, slot_idx, topk_weights):
                 acc = np.float32(acc + np.float32(np.float32(topk_weights[t][k]) * v))
             y[t, h] = acc
     return f32_to_bf16_bits(y)
+
+
+def combine_scatter(expert_out_bits, expand_idx, n_rows, S, K, staging=None):
+    """First pass of the CAM combine ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 7.5
+    CopyBufferToShareAndSetStatus): each expert output row is copied to the token owner's combine
+    buffer at row t*K + k, with (t, k) taken from the triple the row's slot carried. (The page's
+    rows are 512-byte aligned; row spacing does not change the values.)
+
+    expert_out_bits uint16 [>= n_rows, H] (row s = slot s); expand_idx int32 [>= n_rows, 3] holds
+    (src_rank, t, k). Rows whose t or k is out of range are not moved. Returns staging uint16
+    [S*K, H]: the given array updated in place, or a new one with unwritten rows zero.
+    """
+    rows = np.asarray(expert_out_bits, dtype=np.uint16)
+    H = rows.shape[1]
+    out = np.zeros((S * K, H), dtype=np.uint16) if staging is None else staging
+    for s in range(int(n_rows)):
+        t, k = int(expand_idx[s][1]), int(expand_idx[s][2])
+        if 0 <= t < S and 0 <= k < K:
+            out[t * K + k] = rows[s]
+    return out
+
+
+def combine_staged(staging_bits, slot_idx, topk_weights):
+    """Second pass of the CAM combine: token t's K rows are the contiguous rows t*K .. t*K+K-1 of
+    the staging buffer, reduced with the same fp32 arithmetic as `combine`; entries masked in
+    slot_idx (-1) are skipped, as the scatter never filled their rows."""
+    slot_idx = np.asarray(slot_idx)
+    S, K = slot_idx.shape
+    pos = np.arange(S * K, dtype=np.int64).reshape(S, K)
+    return combine(staging_bits, np.where(slot_idx >= 0, pos, -1), topk_weights)

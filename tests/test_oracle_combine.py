@@ -82,3 +82,39 @@ def test_vectorised_equals_bruteforce():
         rows = f32_to_bf16_input(rng.standard_normal((max(R, 1), H)).astype(np.float32))
         wts = rng.random((S, K)).astype(np.float32)
         assert np.array_equal(combine(rows, slot, wts), combine_bruteforce(rows, slot, wts))
+
+
+def test_two_pass_combine_equals_the_gather():
+    """Scattering expert rows to t*K + k by their triples and reducing K contiguous rows gives the
+    same bits as gathering by slot index, on a workload and on tables with masked entries; the
+    staging rows are the expert rows of slot_idx's inverse."""
+    from oracle import combine_scatter, combine_staged, unpack
+
+    cases = [WORKLOADS[1]]
+    for w in cases:
+        inp = make_inputs(w)
+        lay = layout(inp["topk_idx"], w.E, w.P, w.C)
+        slot = lay["slot_idx"]
+        n = int(lay["expert_slot_base"][-1])
+        _, idx, _ = unpack(dispatch_slots(inp["x"], slot, 0, 0), w.H, 0)
+        staging = combine_scatter(inp["expert_out"], idx, n, w.S, w.K)
+        for t in range(w.S):
+            for k in range(w.K):
+                assert np.array_equal(staging[t * w.K + k], inp["expert_out"][slot[t, k]])
+        y2 = combine_staged(staging, slot, inp["topk_weights"])
+        assert np.array_equal(y2, combine(inp["expert_out"], slot, inp["topk_weights"]))
+    rng = np.random.default_rng(12)
+    S, K, E, P, H = 33, 5, 9, 3, 40
+    tab = random_tiny_routing(rng, S, K, E, p_mask=0.3)
+    slot = layout(tab, E, P, 2)["slot_idx"]
+    n = int((slot >= 0).sum())
+    rows = f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))
+    w = rng.random((S, K)).astype(np.float32)
+    idx = np.full((S * K, 3), -1, np.int32)
+    for t, k in zip(*np.nonzero(slot >= 0)):
+        idx[slot[t, k]] = (0, t, k)
+    poison = np.full((S * K, H), 0xFFFF, np.uint16)
+    staging = combine_scatter(rows, idx, n, S, K, staging=poison)
+    assert np.all(staging[(slot < 0).reshape(-1)] == 0xFFFF)  # masked positions never written
+    assert np.array_equal(combine_staged(staging, slot, w), combine(rows, slot, w))
+    assert np.array_equal(combine_staged(staging, slot, w), combine_bruteforce(rows, slot, w))
