@@ -177,6 +177,38 @@ def time_unpack_padded(moe, torch, w, lay, window, n_valid, stream, A=16, iters=
             "GB/s": round(nbytes / avg_us / 1e3, 1), "frac_hbm_peak": round(nbytes / avg_us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def time_two_pass_combine(moe, torch, w, lay, window, inputs, n_valid, gather_bytes, stream, iters=20):
+    """The page's combine form next to the gather: scatter the expert rows to staging row t*K + k
+    by the triples (from moe_unpack of the dispatched window), then reduce K contiguous rows.
+    Outside the timed step; the staging rows are 512-byte aligned as on the page."""
+    x, topk, wts, eo = inputs
+    moe.moe_layout(topk, w.E, w.P, w.C, out=lay)
+    moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+    idx = moe.moe_unpack(window, lay.expert_slot_base[w.E:], w.S, w.K, w.H, w.quant).expand_idx
+    stride = -(-2 * w.H // 512) * 512
+    staging = torch.empty(w.S * w.K * stride, dtype=torch.uint8, device=eo.device)
+    y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=eo.device)
+    t_sc, t_st = [], []
+    for i in range(iters + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        moe.moe_combine_scatter(eo, idx, lay.expert_slot_base[w.E:], w.S, w.K, staging=staging,
+                                staging_stride_bytes=stride)
+        e[1].record(stream)
+        moe.moe_combine_staged(staging, lay.slot_idx, wts, w.H, staging_stride_bytes=stride, y=y)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            t_sc.append(e[0].elapsed_time(e[1]))
+            t_st.append(e[1].elapsed_time(e[2]))
+    sc_bytes = n_valid * (2 * w.H + 2 * w.H + 12) + 4
+    sc_us, st_us = 1e3 * float(np.mean(t_sc)), 1e3 * float(np.mean(t_st))
+    return {"scatter_us": round(sc_us, 2), "scatter_bytes": sc_bytes,
+            "scatter_GB/s": round(sc_bytes / sc_us / 1e3, 1),
+            "staged_us": round(st_us, 2), "staged_GB/s": round(gather_bytes / st_us / 1e3, 1),
+            "total_us": round(sc_us + st_us, 2)}
+
+
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
     """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
     payload = 2 * w.H if w.quant == 0 else w.H
@@ -356,6 +388,8 @@ def main():
                                                           total_bytes)
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
+        out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],
+                                                                  n_valid, nbytes["combine"], stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

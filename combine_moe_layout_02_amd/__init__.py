@@ -30,7 +30,8 @@ MOE_QUANT_INT8_DYN = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
-    "moe_combine", "moe_unpack", "moe_unpack_padded", "moe_status_string",
+    "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "moe_unpack_padded",
+    "moe_status_string",
 )
 
 
@@ -53,6 +54,8 @@ def _load():
         "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
+        "moe_combine_scatter": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, I64, I64, P]),
+        "moe_combine_staged": (ctypes.c_int, [P, I64, P, P, I32, I32, I32, P, P]),
         "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
         "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
                                              P, P, P, P, P, P]),
@@ -224,6 +227,54 @@ def moe_combine(expert_out, slot_idx, topk_weights, row_stride_bytes=None, exper
     return y
 
 
+def moe_combine_scatter(expert_out, expand_idx, num_rows, S, K, staging=None, staging_stride_bytes=None,
+                        stream=None):
+    """First pass of the two-pass combine: bf16 expert rows [R, H] (row s for slot s) to staging
+    row t*K + k by their triples expand_idx [R, 3]; rows at or past the device count num_rows are
+    skipped. staging defaults to a new bf16 [S*K, H] tensor (stride 2H)."""
+    _need(expert_out, "expert_out", torch.bfloat16, 2)
+    dev = expert_out.device
+    _need(expand_idx, "expand_idx", torch.int32, 2, dev)
+    _need(num_rows, "num_rows", torch.int32, device=dev)
+    R, H = expert_out.shape
+    S, K = int(S), int(K)
+    if tuple(expand_idx.shape) != (R, 3):
+        raise ValueError("expand_idx must be [rows of expert_out, 3]")
+    if staging is None:
+        staging = torch.empty((S * K, H), dtype=torch.bfloat16, device=dev)
+    _need(staging, "staging", device=dev)
+    stride = 2 * H if staging_stride_bytes is None else int(staging_stride_bytes)
+    _check(_lib.moe_combine_scatter(_ptr(expert_out), 2 * H, R, _ptr(expand_idx), _ptr(num_rows), S, K,
+                                    H, _ptr(staging), stride, staging.numel() * staging.element_size(),
+                                    _stream(dev, stream)))
+    return staging
+
+
+def moe_combine_staged(staging, slot_idx, topk_weights, hidden, staging_stride_bytes=None, y=None,
+                       stream=None):
+    """Second pass of the two-pass combine: y[t] reduces staging rows t*K .. t*K+K-1 (entries with
+    slot_idx < 0 skipped) with the arithmetic of moe_combine."""
+    _need(slot_idx, "slot_idx", torch.int32, 2)
+    dev = slot_idx.device
+    _need(staging, "staging", device=dev)
+    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
+    S, K = slot_idx.shape
+    H = int(hidden)
+    stride = 2 * H if staging_stride_bytes is None else int(staging_stride_bytes)
+    if tuple(topk_weights.shape) != (S, K):
+        raise ValueError("topk_weights must match slot_idx")
+    if ((S * K - 1) * stride + 2 * H) > staging.numel() * staging.element_size():
+        raise ValueError("staging must hold S*K rows of the given stride")
+    if y is None:
+        y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, 2, dev)
+    if tuple(y.shape) != (S, H):
+        raise ValueError(f"y must have shape {(S, H)}")
+    _check(_lib.moe_combine_staged(_ptr(staging), stride, _ptr(slot_idx), _ptr(topk_weights), S, H, K,
+                                   _ptr(y), _stream(dev, stream)))
+    return y
+
+
 class Unpacked(NamedTuple):
     expand_x: torch.Tensor  # [S*K, H] bf16, or uint8 codes for the quantised modes
     expand_scales: torch.Tensor  # fp32 [S*K] (quantised modes) or None
@@ -316,6 +367,6 @@ __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_combine", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_status_string",
 ]

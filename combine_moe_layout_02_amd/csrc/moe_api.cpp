@@ -113,6 +113,43 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
                                         topk_weights, S, H, K, y, stream));
 }
 
+int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
+                        const int32_t *expand_idx, const int32_t *num_rows, int32_t S, int32_t K,
+                        int32_t H, void *staging, int64_t staging_stride_bytes,
+                        int64_t staging_bytes, hipStream_t stream) {
+    if (!expert_out || !expand_idx || !num_rows || !staging) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (expert_rows < 0 || expert_rows > MOE_MAX_OUT_ROWS) return MOE_ERR_ARG;
+    if (row_stride_bytes < 2 * (int64_t)H || staging_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
+    if (row_stride_bytes % 16 != 0 || staging_stride_bytes % 16 != 0 || !aligned(expert_out, 16) ||
+        !aligned(staging, 16) || !aligned(expand_idx, 4) || !aligned(num_rows, 4))
+        return MOE_ERR_ALIGN;
+    if (staging_bytes < ((int64_t)S * K - 1) * staging_stride_bytes + 2 * (int64_t)H)
+        return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_combine_scatter(expert_out, row_stride_bytes, expert_rows,
+                                                expand_idx, num_rows, S, K, H, staging,
+                                                staging_stride_bytes, stream));
+}
+
+int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const int32_t *slot_idx,
+                       const float *topk_weights, int32_t S, int32_t H, int32_t K, void *y,
+                       hipStream_t stream) {
+    if (!staging || !slot_idx || !topk_weights || !y) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (staging_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
+    if (staging_stride_bytes % 16 != 0 || !aligned(staging, 16) || !aligned(y, 16) ||
+        !aligned(slot_idx, 4) || !aligned(topk_weights, 4))
+        return MOE_ERR_ALIGN;
+    return from_hip(moe::launch_combine_staged(staging, staging_stride_bytes, slot_idx,
+                                               topk_weights, S, H, K, y, stream));
+}
+
 int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,
                int32_t K, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
                int32_t *expand_idx, hipStream_t stream) {

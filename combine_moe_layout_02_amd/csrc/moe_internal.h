@@ -64,6 +64,15 @@ hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int6
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,
                           int32_t H, int32_t K, void *y, hipStream_t stream);
 
+hipError_t launch_combine_scatter(const void *expert_out, int64_t row_stride_bytes,
+                                  int64_t expert_rows, const int32_t *expand_idx,
+                                  const int32_t *num_rows, int32_t S, int32_t K, int32_t H,
+                                  void *staging, int64_t staging_stride_bytes, hipStream_t stream);
+
+hipError_t launch_combine_staged(const void *staging, int64_t staging_stride_bytes,
+                                 const int32_t *slot_idx, const float *topk_weights, int32_t S,
+                                 int32_t H, int32_t K, void *y, hipStream_t stream);
+
 hipError_t launch_unpack_padded(const void *window, const int32_t *expert_slot_base, int32_t E,
                                 int32_t S, int32_t K, int32_t H, int32_t quant,
                                 int32_t expert_alignment, int64_t out_rows, void *expand_x,

@@ -156,6 +156,38 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
                 const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
                 int32_t K, void *y, hipStream_t stream);
 
+/* Two-pass combine, the CAM form of the combine ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", sections
+ * 7.5 CopyBufferToShareAndSetStatus and 7.8 ReadBufferAndWeightedSum): first every expert output
+ * row is copied to position t*K + k of a staging buffer, (t, k) taken from the triple its slot
+ * carried; then each token reduces its K contiguous staging rows with the arithmetic of
+ * moe_combine. moe_combine_staged(moe_combine_scatter(...)) gives bit for bit what moe_combine
+ * gives on the same rows; the two-pass form moves each row twice more and exists to compare the
+ * page's design with the single gather.
+ *
+ * moe_combine_scatter
+ * In:  expert_out     bf16 rows as for moe_combine (row s = the output for slot s); expert_rows
+ *                     rows are readable, expert_rows in [0, MOE_MAX_OUT_ROWS].
+ *      expand_idx     int32 [expert_rows, 3]: the (src_rank, t, k) triple of each row, e.g. from
+ *                     moe_unpack.
+ *      num_rows       DEVICE pointer to N (e.g. &expert_slot_base[E]); rows s >= min(N,
+ *                     expert_rows) and rows whose (t, k) lies outside [0, S) x [0, K) are not moved.
+ * Out: staging        bf16, row t*K + k at byte offset (t*K + k) * staging_stride_bytes (stride
+ *                     >= 2H, multiple of 16; the page uses rows rounded up to 512 bytes);
+ *                     staging_bytes must cover S*K rows. Rows that receive nothing keep their
+ *                     contents.
+ * moe_combine_staged
+ * In:  staging as written by moe_combine_scatter; slot_idx int32 [S, K] (only its sign is used:
+ *      entries < 0 are skipped, all others read staging row t*K + k); topk_weights fp32 [S, K].
+ * Out: y bf16 [S, H], fully overwritten. */
+int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
+                        const int32_t *expand_idx, const int32_t *num_rows, int32_t S, int32_t K,
+                        int32_t H, void *staging, int64_t staging_stride_bytes,
+                        int64_t staging_bytes, hipStream_t stream);
+
+int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const int32_t *slot_idx,
+                       const float *topk_weights, int32_t S, int32_t H, int32_t K, void *y,
+                       hipStream_t stream);
+
 /* Unpack: window slots -> compact expert input rows ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析",
  * section 3.9 ShareToOutput, which copies each received slot's token data to the next row of
  * expandXOut and its triple to expandIdxOut). On one GPU the window is already expert-major with

@@ -188,3 +188,47 @@ def unpack_padded_call(win=A, nbytes=None, esb=A, E=256, S=64, K=8, H=7168, quan
 ])
 def test_unpack_padded_validation(kw, err):
     assert unpack_padded_call(**kw) == err
+
+
+def scatter_call(eo=A, stride=14336, rows=512, idx=A, num=A, S=64, K=8, H=7168, stg=A,
+                 sstride=14336, sbytes=None):
+    if sbytes is None:
+        sbytes = S * K * sstride
+    return moe._lib.moe_combine_scatter(eo, stride, rows, idx, num, S, K, H, stg, sstride, sbytes, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(eo=NULL), moe.MOE_ERR_ARG),
+    (dict(idx=NULL), moe.MOE_ERR_ARG),
+    (dict(num=NULL), moe.MOE_ERR_ARG),
+    (dict(stg=NULL), moe.MOE_ERR_ARG),
+    (dict(rows=-1), moe.MOE_ERR_ARG),
+    (dict(rows=1048577), moe.MOE_ERR_ARG),
+    (dict(stride=14320), moe.MOE_ERR_ARG),
+    (dict(sstride=14320, sbytes=10**9), moe.MOE_ERR_ARG),
+    (dict(sstride=14344, sbytes=10**9), moe.MOE_ERR_ALIGN),
+    (dict(stg=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(idx=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(sbytes=(64 * 8 - 1) * 14336 + 2 * 7168 - 1), moe.MOE_ERR_WINDOW),
+    (dict(H=7176), moe.MOE_ERR_UNSUPPORTED),
+    (dict(K=17), moe.MOE_ERR_ARG),
+])
+def test_combine_scatter_validation(kw, err):
+    assert scatter_call(**kw) == err
+
+
+def staged_call(stg=A, sstride=14336, slot=A, w=A, S=64, H=7168, K=8, y=A):
+    return moe._lib.moe_combine_staged(stg, sstride, slot, w, S, H, K, y, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(stg=NULL), moe.MOE_ERR_ARG),
+    (dict(y=NULL), moe.MOE_ERR_ARG),
+    (dict(sstride=14000), moe.MOE_ERR_ARG),
+    (dict(sstride=14344), moe.MOE_ERR_ALIGN),
+    (dict(y=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(w=A + 1), moe.MOE_ERR_ALIGN),
+    (dict(S=0), moe.MOE_ERR_ARG),
+])
+def test_combine_staged_validation(kw, err):
+    assert staged_call(**kw) == err

@@ -428,6 +428,67 @@ def test_combine_tiny(moe, case):
     assert np.array_equal(got, ref), f"{case}: within 1 ulp but not bit-exact"
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_two_pass_combine_workloads(moe, cfg):
+    """Scatter by the unpacked triples, then the staged reduction: staging rows and y bit for bit
+    against the oracle's two passes (and so against the gather combine)."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
+    slot = lay.slot_idx.cpu().numpy()
+    n = int(lay.expert_slot_base[w.E].item())
+    win = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(bf16_dev(inp["x"]), lay.slot_idx, win, 0, 0)
+    un = moe.moe_unpack(win, lay.expert_slot_base[w.E:], w.S, w.K, w.H, 0)
+    eo = expert_out(cfg)
+    wts = to_dev(inp["topk_weights"])
+    stride = -(-2 * w.H // 512) * 512  # the page's 512-byte rows
+    staging = torch.full((w.S * w.K * stride,), POISON, dtype=torch.uint8, device=DEV)
+    note(f"two-pass combine cfg{cfg} {w.describe()}")
+    moe.moe_combine_scatter(bf16_dev(eo[: w.S * w.K]), un.expand_idx, lay.expert_slot_base[w.E:], w.S,
+                            w.K, staging=staging, staging_stride_bytes=stride)
+    y = moe.moe_combine_staged(staging, lay.slot_idx, wts, w.H, staging_stride_bytes=stride)
+    torch.cuda.synchronize()
+    idx = un.expand_idx.cpu().numpy()
+    ref_stg = oracle.combine_scatter(eo, idx, n, w.S, w.K)
+    got_stg = staging.view(w.S * w.K, stride).cpu().numpy()[:, : 2 * w.H].view(np.uint16)
+    live = (slot >= 0).reshape(-1)
+    assert np.array_equal(got_stg[live], ref_stg[live])
+    assert np.all(got_stg[~live].view(np.uint8) == POISON)  # masked positions never written
+    ref_y = oracle.combine_staged(ref_stg, slot, inp["topk_weights"])
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref_y)
+    assert np.array_equal(ref_y, oracle.combine(eo, slot, inp["topk_weights"]))
+
+
+def test_two_pass_combine_masked_and_partial(moe):
+    """Masked entries and N below the row count: skipped rows move nothing; y still matches."""
+    rng = np.random.default_rng(44)
+    S, K, E, P, H = 70, 6, 10, 5, 272
+    tab = random_tiny_routing(rng, S, K, E, p_mask=0.35)
+    lay = moe.moe_layout(to_dev(tab), E, P, 4)
+    slot = lay.slot_idx.cpu().numpy()
+    n = int((slot >= 0).sum())
+    rows = f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))
+    wts = rng.random((S, K)).astype(np.float32)
+    idx = np.full((S * K, 3), -1, np.int32)
+    for t, k in zip(*np.nonzero(slot >= 0)):
+        idx[slot[t, k]] = (0, t, k)
+    full = None
+    for n_dev in (n, n // 2, 0):
+        staging = torch.full((S * K, H), -7, dtype=torch.int16, device=DEV)
+        nd = torch.tensor([n_dev], dtype=torch.int32, device=DEV)
+        moe.moe_combine_scatter(bf16_dev(rows), to_dev(idx), nd, S, K, staging=staging)
+        torch.cuda.synchronize()
+        ref = oracle.combine_scatter(rows, idx, n_dev, S, K,
+                                     staging=np.full((S * K, H), 0xFFF9, np.uint16))
+        assert np.array_equal(staging.cpu().numpy().view(np.uint16), ref), n_dev
+        if full is None:
+            full = staging
+    y = moe.moe_combine_staged(full, lay.slot_idx, to_dev(wts), H)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), oracle.combine(rows, slot, wts))
+
+
 def test_combine_from_window_round_trip(moe):
     """Identity experts: combine read straight from the bf16 window returns x (weights sum to 1)."""
     w = WORKLOADS[3]
