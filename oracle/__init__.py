@@ -16,7 +16,8 @@ written out step by step. Citations name the page title and the section on it:
 * "Ascend DeepEP MoE Dispatch Optimization": "一条 token 如何走完 MoE" (token path,
   dst_rank), "Dispatch handle 六项分别保存什么" (handle tensors), "Notify 先交换数量和前缀"
   (counts and prefix sums), "Device 侧如何把 channel 变成远端 Put" (per-channel cursor),
-  "所谓 compact plan 到底压缩了什么" (compact destination plan), "输出长度有动态和固定两种模式"
+  "所谓 compact plan 到底压缩了什么" (compact destination plan), "P 维路由为什么值得单独优化"
+  (per-destination segments), "输出长度有动态和固定两种模式"
   (fixed-length num_worst_tokens outputs).
 * "internode.cu", section 1 notify_dispatch (per-rank / per-expert counting, the
   expert_alignment rounding of the per-expert counts).
@@ -42,6 +43,7 @@ from .dispatch import (
 )
 from .combine import combine, combine_bruteforce, combine_scatter, combine_staged
 from .unpack import aligned_row_base, unpack, unpack_padded
+from .dedup import dispatch_dedup, expand_dedup, rank_rows
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -64,4 +66,7 @@ __all__ = [
     "unpack",
     "aligned_row_base",
     "unpack_padded",
+    "rank_rows",
+    "dispatch_dedup",
+    "expand_dedup",
 ]
