@@ -209,6 +209,45 @@ def time_two_pass_combine(moe, torch, w, lay, window, inputs, n_valid, gather_by
             "total_us": round(sc_us + st_us, 2)}
 
 
+def time_dedup(moe, torch, w, C, lay, window, inputs, n_valid, kfold_pack_bytes, stream, iters=20):
+    """DeepEP's per-rank deduplicated dispatch next to the K-fold pack: rank rows, the dedup pack
+    (one row per token and destination rank) and the receive-side expansion to expert-major rows
+    (which equals moe_unpack of the K-fold window). Outside the timed step; reuses the window."""
+    x, topk, wts, eo = inputs
+    moe.moe_layout(topk, w.E, w.P, C, out=lay)
+    rr = moe.moe_rank_rows(topk, lay, w.E, w.P, C)
+    exp = moe.moe_expand_dedup(window, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H)
+    torch.cuda.synchronize()
+    m = int(rr.rank_token_base[w.P].item())
+    ms = {"rank_rows": [], "dispatch_dedup": [], "expand_dedup": []}
+    for i in range(iters + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        moe.moe_rank_rows(topk, lay, w.E, w.P, C, out=rr)
+        e[1].record(stream)
+        moe.moe_dispatch_dedup(x, rr.rank_row_idx, topk, w.E, w.P, window)
+        e[2].record(stream)
+        moe.moe_expand_dedup(window, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H,
+                             out=exp)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            for j, k in enumerate(ms):
+                ms[k].append(e[j].elapsed_time(e[j + 1]))
+    row = 2 * w.H + 12
+    pack_bytes = 2 * w.S * w.H + 8 * w.S * w.K + m * row
+    expand_bytes = m * row + n_valid * row + 4 * w.S * w.K + 8 * n_valid + 4
+    out = {"rows": m, "rows_per_token": round(m / w.S, 3),
+           "write_bytes_vs_kfold": round(m / n_valid, 4)}
+    for k, nb in (("rank_rows", None), ("dispatch_dedup", pack_bytes), ("expand_dedup", expand_bytes)):
+        us = 1e3 * float(np.mean(ms[k]))
+        out[k] = {"avg_us": round(us, 2)}
+        if nb:
+            out[k].update({"bytes": nb, "GB/s": round(nb / us / 1e3, 1),
+                           "frac_hbm_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)})
+    return out
+
+
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
     """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
     payload = 2 * w.H if w.quant == 0 else w.H
@@ -390,6 +429,9 @@ def main():
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],
                                                                   n_valid, nbytes["combine"], stream)
+        if w.quant == 0:
+            out["extras"]["dedup_dispatch"] = time_dedup(moe, torch, w, C, lay, window, sets[0], n_valid,
+                                                         nbytes["dispatch"], stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

@@ -31,6 +31,7 @@ MOE_QUANT_INT8_DYN = 2
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
     "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "moe_unpack_padded",
+    "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 )
 
@@ -57,6 +58,10 @@ def _load():
         "moe_combine_scatter": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, I64, I64, P]),
         "moe_combine_staged": (ctypes.c_int, [P, I64, P, P, I32, I32, I32, P, P]),
         "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
+        "moe_dedup_window_bytes": (I64, [I32, I32, I32, I32]),
+        "moe_rank_rows": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P]),
+        "moe_dispatch_dedup": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P]),
+        "moe_expand_dedup": (ctypes.c_int, [P, I64, P, P, P, I32, I32, I32, I32, P, P, P]),
         "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
                                              P, P, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -275,6 +280,89 @@ def moe_combine_staged(staging, slot_idx, topk_weights, hidden, staging_stride_b
     return y
 
 
+def moe_dedup_window_bytes(S, K, P, H):
+    v = _lib.moe_dedup_window_bytes(int(S), int(K), int(P), int(H))
+    if v < 0:
+        _check(int(v))
+    return int(v)
+
+
+class RankRows(NamedTuple):
+    rank_row_idx: torch.Tensor  # int32 [S, K]
+    rank_token_base: torch.Tensor  # int32 [P + 1]
+
+
+def moe_rank_rows(topk_idx, layout, num_experts, num_ranks, num_channels, out=None, stream=None):
+    """Per-rank deduplicated rows of the routing table, from moe_layout's rank_prefix_matrix and
+    num_tokens_per_rank (layout is the Layout moe_layout returned)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    dev = topk_idx.device
+    S, K = topk_idx.shape
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    _need(layout.rank_prefix_matrix, "rank_prefix_matrix", torch.int32, 2, dev)
+    _need(layout.num_tokens_per_rank, "num_tokens_per_rank", torch.int32, 1, dev)
+    if tuple(layout.rank_prefix_matrix.shape) != (P, C) or layout.num_tokens_per_rank.shape[0] != P:
+        raise ValueError("layout does not match num_ranks / num_channels")
+    if out is None:
+        out = RankRows(torch.empty((S, K), dtype=torch.int32, device=dev),
+                       torch.empty(P + 1, dtype=torch.int32, device=dev))
+    _need(out.rank_row_idx, "rank_row_idx", torch.int32, 2, dev)
+    _need(out.rank_token_base, "rank_token_base", torch.int32, 1, dev)
+    if tuple(out.rank_row_idx.shape) != (S, K) or out.rank_token_base.shape[0] != P + 1:
+        raise ValueError("rank_row_idx must be [S, K] and rank_token_base [P + 1]")
+    _check(_lib.moe_rank_rows(_ptr(topk_idx), S, K, E, P, C, _ptr(layout.rank_prefix_matrix),
+                              _ptr(layout.num_tokens_per_rank), _ptr(out.rank_row_idx),
+                              _ptr(out.rank_token_base), _stream(dev, stream)))
+    return out
+
+
+def moe_dispatch_dedup(x, rank_row_idx, topk_idx, num_experts, num_ranks, window, src_rank=0,
+                       stream=None):
+    """One bf16 row per (token, destination rank) into the rows named by rank_row_idx."""
+    _need(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _need(rank_row_idx, "rank_row_idx", torch.int32, 2, dev)
+    _need(topk_idx, "topk_idx", torch.int32, 2, dev)
+    _need(window, "window", device=dev)
+    S, H = x.shape
+    K = topk_idx.shape[1]
+    if tuple(topk_idx.shape) != (S, K) or tuple(rank_row_idx.shape) != (S, K):
+        raise ValueError("rank_row_idx and topk_idx must be [S, K] with S rows of x")
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_dispatch_dedup(_ptr(x), _ptr(rank_row_idx), _ptr(topk_idx), S, H, K,
+                                   int(num_experts), int(num_ranks), int(src_rank), _ptr(window),
+                                   nbytes, _stream(dev, stream)))
+    return window
+
+
+def moe_expand_dedup(window, rank_row_idx, slot_idx, num_slots, num_ranks, H, out=None, stream=None):
+    """Receive-side expansion of the deduplicated rows to the expert-major rows of slot_idx:
+    returns (expand_x bf16 [S*K, H], expand_idx int32 [S*K, 3]) as moe_unpack would. num_slots
+    is the device count N (layout.expert_slot_base[E:])."""
+    _need(window, "window")
+    dev = window.device
+    _need(rank_row_idx, "rank_row_idx", torch.int32, 2, dev)
+    _need(slot_idx, "slot_idx", torch.int32, 2, dev)
+    _need(num_slots, "num_slots", torch.int32, device=dev)
+    S, K = slot_idx.shape
+    H = int(H)
+    if tuple(rank_row_idx.shape) != (S, K):
+        raise ValueError("rank_row_idx must match slot_idx")
+    if out is None:
+        out = (torch.empty((S * K, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((S * K, 3), dtype=torch.int32, device=dev))
+    ex, idx = out
+    _need(ex, "expand_x", device=dev)
+    _need(idx, "expand_idx", torch.int32, 2, dev)
+    if ex.numel() * ex.element_size() < S * K * 2 * H or tuple(idx.shape) != (S * K, 3):
+        raise ValueError("expand_x must hold S*K rows of 2H bytes and expand_idx [S*K, 3]")
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_expand_dedup(_ptr(window), nbytes, _ptr(rank_row_idx), _ptr(slot_idx),
+                                 _ptr(num_slots), S, K, int(num_ranks), H, _ptr(ex), _ptr(idx),
+                                 _stream(dev, stream)))
+    return out
+
+
 class Unpacked(NamedTuple):
     expand_x: torch.Tensor  # [S*K, H] bf16, or uint8 codes for the quantised modes
     expand_scales: torch.Tensor  # fp32 [S*K] (quantised modes) or None
@@ -368,5 +456,6 @@ __all__ = [
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
     "moe_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 ]

@@ -275,6 +275,127 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     if (bad) atomicOr(status, 1);
 }
 
+// Value of v held by the first lane of this token whose rank equals r (lanes lk - J for J = 1..KP-1
+// are the lower lanes of the same token; DPP reads them within the 16-lane row). Lanes that are
+// themselves the first keep v. Called with every lane of the wave active.
+template <int KP, int J = 1>
+__device__ inline int first_lane_value(int v, int r, bool first, int lk, int found) {
+    if constexpr (J >= KP) {
+        return first ? v : found;
+    } else {
+        const int rj = __builtin_amdgcn_update_dpp(-2, r, 0x110 + J, 0xF, 0xF, false);
+        const int vj = __builtin_amdgcn_update_dpp(0, v, 0x110 + J, 0xF, 0xF, false);
+        const int fj = __builtin_amdgcn_update_dpp(0, first ? 1 : 0, 0x110 + J, 0xF, 0xF, false);
+        const bool hit = (J <= lk) & (rj == r) & (fj != 0);
+        return first_lane_value<KP, J + 1>(v, r, first, lk, hit ? vj : found);
+    }
+}
+
+// Per-rank deduplicated rows ("Ascend DeepEP MoE Dispatch Optimization", sections "一条 token 如何走完
+// MoE" and "所谓 compact plan 到底压缩了什么": one copy of a token per destination rank, grouped into
+// one segment per rank). Rank r's segment starts at rank_token_base[r] (exclusive prefix of
+// num_tokens_per_rank) and lists its tokens in ascending order, so token t's row on rank r is
+//   rank_token_base[r] + rank_prefix[r][c-1] (tokens of r in earlier channels)
+//                      + tokens of r earlier in channel c.
+// One workgroup per channel, lanes over (token, k) as in the count kernel; the first lane of each
+// (token, rank) gets its order from per-wave lane masks + popcount, and the token's other lanes on
+// the same rank copy it with DPP. Workgroup 0 also writes rank_token_base.
+template <int KP>
+__global__ __launch_bounds__(kThreads) void rank_rows_kernel(
+    const int32_t *__restrict__ topk, int S, int K, int E, int P, int epr, int C,
+    const int32_t *__restrict__ rank_prefix, const int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ rank_row_idx, int32_t *__restrict__ rank_token_base) {
+    constexpr int kTokWave = 64 / KP;
+    constexpr int kTokBatch = kWaves * kTokWave;
+    __shared__ int32_t rbase[MOE_MAX_RANKS];
+    __shared__ int32_t rank_run[MOE_MAX_RANKS];
+    __shared__ int32_t wave_sum[kWaves];
+    __shared__ unsigned long long lane_mask[kWaves][MOE_MAX_RANKS];
+
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tl = wave * kTokWave + lane / KP;
+    const int lk = lane % KP;
+    int tb, te;
+    channel_range(S, C, c, tb, te);
+
+    // segment starts: exclusive scan of num_tokens_per_rank, two ranks per lane (P <= 512)
+    const int r0 = 2 * tid, r1 = 2 * tid + 1;
+    const int n0 = r0 < P ? num_tokens_per_rank[r0] : 0;
+    const int n1 = r1 < P ? num_tokens_per_rank[r1] : 0;
+    const int pair = n0 + n1;
+    const int incl = wave_inclusive_scan(pair, lane);
+    if (lane == 63) wave_sum[wave] = incl;
+    for (int r = tid; r < P; r += kThreads) {
+        rank_run[r] = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) lane_mask[w][r] = 0ull;
+    }
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        before += w < wave ? wave_sum[w] : 0;
+        total += wave_sum[w];
+    }
+    const int b0 = before + incl - pair, b1 = b0 + n0;
+    if (r0 < P) rbase[r0] = b0 + (c > 0 ? rank_prefix[(int64_t)r0 * C + c - 1] : 0);
+    if (r1 < P) rbase[r1] = b1 + (c > 0 ? rank_prefix[(int64_t)r1 * C + c - 1] : 0);
+    if (c == 0) {
+        if (r0 < P) rank_token_base[r0] = b0;
+        if (r1 < P) rank_token_base[r1] = b1;
+        if (tid == 0) rank_token_base[P] = total;
+    }
+
+    const unsigned long long lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    auto fetch = [&](int t0) {
+        const int t = t0 + tl;
+        return (t < te && lk < K) ? topk[(int64_t)t * K + lk] : -1;
+    };
+    int next = fetch(tb);
+    __syncthreads();
+    for (int t0 = tb; t0 < te; t0 += kTokBatch) {
+        const int v = next;
+        next = fetch(t0 + kTokBatch);
+        const int t = t0 + tl;
+        const int r = (v >= 0 && v < E) ? v / epr : -1;
+        const bool first = first_in_token<KP>(r, lk);
+        if (first) atomicOr(&lane_mask[wave][r], 1ull << lane);
+        __syncthreads();
+        int order = 0, count = 0;
+        bool leader = false;
+        if (first) {
+            int earlier = 0;
+            for (int w = 0; w < wave; ++w) earlier += __popcll(lane_mask[w][r]);
+            const int below = __popcll(lane_mask[wave][r] & lt_mask);
+            order = rank_run[r] + earlier + below;
+            leader = earlier == 0 && below == 0;  // first token of rank r in this batch
+            if (leader)
+                for (int w = 0; w < kWaves; ++w) count += __popcll(lane_mask[w][r]);
+        }
+        const int row = (r >= 0 ? rbase[r] : 0) + order;
+        const int mine = first_lane_value<KP>(row, r, first, lk, 0);
+        if (t < te && lk < K) rank_row_idx[(int64_t)t * K + lk] = r >= 0 ? mine : -1;
+        __syncthreads();
+        if (first) {
+            if (leader) rank_run[r] += count;
+            lane_mask[wave][r] = 0ull;
+        }
+        __syncthreads();
+    }
+}
+
+template <int KP>
+hipError_t launch_rank_rows_kp(const int32_t *topk_idx, int S, int K, int E, int P, int C,
+                               const int32_t *rank_prefix, const int32_t *num_tokens_per_rank,
+                               int32_t *rank_row_idx, int32_t *rank_token_base,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(rank_rows_kernel<KP>, dim3(C), dim3(kThreads), 0, stream, topk_idx, S, K, E,
+                       P, E / P, C, rank_prefix, num_tokens_per_rank, rank_row_idx,
+                       rank_token_base);
+    return hipGetLastError();
+}
+
 template <int KP>
 hipError_t launch_count(const int32_t *topk_idx, int S, int K, int E, int P, int C,
                         uint8_t *is_in, int32_t *rank_prefix, int32_t *expert_prefix,
@@ -324,6 +445,21 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
                        expert_slot_base, rank_slot_base, num_tokens_per_expert,
                        num_tokens_per_rank, status);
     return hipGetLastError();
+}
+
+hipError_t launch_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                            int32_t C, const int32_t *rank_prefix_matrix,
+                            const int32_t *num_tokens_per_rank, int32_t *rank_row_idx,
+                            int32_t *rank_token_base, hipStream_t stream) {
+    if (K <= 1)
+        return launch_rank_rows_kp<1>(topk_idx, S, K, E, P, C, rank_prefix_matrix, num_tokens_per_rank, rank_row_idx, rank_token_base, stream);
+    if (K <= 2)
+        return launch_rank_rows_kp<2>(topk_idx, S, K, E, P, C, rank_prefix_matrix, num_tokens_per_rank, rank_row_idx, rank_token_base, stream);
+    if (K <= 4)
+        return launch_rank_rows_kp<4>(topk_idx, S, K, E, P, C, rank_prefix_matrix, num_tokens_per_rank, rank_row_idx, rank_token_base, stream);
+    if (K <= 8)
+        return launch_rank_rows_kp<8>(topk_idx, S, K, E, P, C, rank_prefix_matrix, num_tokens_per_rank, rank_row_idx, rank_token_base, stream);
+    return launch_rank_rows_kp<16>(topk_idx, S, K, E, P, C, rank_prefix_matrix, num_tokens_per_rank, rank_row_idx, rank_token_base, stream);
 }
 
 }  // namespace moe

@@ -28,6 +28,12 @@ int check_tokens(int32_t S, int32_t K) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+int check_experts(int32_t E, int32_t P) {
+    if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (E % P != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -44,6 +50,15 @@ int64_t moe_window_bytes(int32_t S, int32_t K, int32_t H) {
     st = check_tokens(S, K);
     if (st != MOE_OK) return st;
     return (int64_t)S * K * moe::slot_geom(H, MOE_QUANT_NONE).slot_bytes;
+}
+
+int64_t moe_dedup_window_bytes(int32_t S, int32_t K, int32_t P, int32_t H) {
+    int st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    if (P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    return (int64_t)S * (K < P ? K : P) * moe::slot_geom(H, MOE_QUANT_NONE).slot_bytes;
 }
 
 int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *scale_off,
@@ -148,6 +163,61 @@ int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const 
         return MOE_ERR_ALIGN;
     return from_hip(moe::launch_combine_staged(staging, staging_stride_bytes, slot_idx,
                                                topk_weights, S, H, K, y, stream));
+}
+
+int moe_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                  const int32_t *rank_prefix_matrix, const int32_t *num_tokens_per_rank,
+                  int32_t *rank_row_idx, int32_t *rank_token_base, hipStream_t stream) {
+    if (!topk_idx || !rank_prefix_matrix || !num_tokens_per_rank || !rank_row_idx ||
+        !rank_token_base)
+        return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_experts(E, P);
+    if (st != MOE_OK) return st;
+    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(rank_prefix_matrix, 4) ||
+        !aligned(num_tokens_per_rank, 4) || !aligned(rank_row_idx, 4) || !aligned(rank_token_base, 4))
+        return MOE_ERR_ALIGN;
+    return from_hip(moe::launch_rank_rows(topk_idx, S, K, E, P, C, rank_prefix_matrix,
+                                          num_tokens_per_rank, rank_row_idx, rank_token_base,
+                                          stream));
+}
+
+int moe_dispatch_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
+                       int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t src_rank,
+                       void *window, int64_t window_bytes, hipStream_t stream) {
+    if (!x || !rank_row_idx || !topk_idx || !window) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    st = check_experts(E, P);
+    if (st != MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(window, 512) || !aligned(rank_row_idx, 4) || !aligned(topk_idx, 4))
+        return MOE_ERR_ALIGN;
+    if (window_bytes < moe_dedup_window_bytes(S, K, P, H)) return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_pack_dedup(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank,
+                                           window, stream));
+}
+
+int moe_expand_dedup(const void *window, int64_t window_bytes, const int32_t *rank_row_idx,
+                     const int32_t *slot_idx, const int32_t *num_slots, int32_t S, int32_t K,
+                     int32_t P, int32_t H, void *expand_x, int32_t *expand_idx,
+                     hipStream_t stream) {
+    if (!window || !rank_row_idx || !slot_idx || !num_slots || !expand_x || !expand_idx)
+        return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (!aligned(window, 512) || !aligned(expand_x, 16) || !aligned(rank_row_idx, 4) ||
+        !aligned(slot_idx, 4) || !aligned(num_slots, 4) || !aligned(expand_idx, 4))
+        return MOE_ERR_ALIGN;
+    if (window_bytes < moe_dedup_window_bytes(S, K, P, H)) return MOE_ERR_WINDOW;
+    return from_hip(moe::launch_expand_dedup(window, rank_row_idx, slot_idx, num_slots, S, K, P, H,
+                                             expand_x, expand_idx, stream));
 }
 
 int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,

@@ -60,7 +60,9 @@ __device__ inline void store_tail(__amdgpu_buffer_rsrc_t slot, const SlotGeom &g
 }
 
 // grid = S * nparts; workgroup (t, q) copies vectors [q*kPartThreads, (q+1)*kPartThreads) of
-// x[t] into the K slots of token t; the last part also writes the slot tails.
+// x[t] into the K slots of token t; the last part also writes the slot tails. (Loading the K slot
+// indices up front and unrolling the K stores was measured slower here: 114 us against 101 us at
+// S=4096, H=7168, K=8.)
 __global__ __launch_bounds__(kPartThreads) void pack_bf16_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int nvec,
     int nparts, SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
@@ -79,6 +81,46 @@ __global__ __launch_bounds__(kPartThreads) void pack_bf16_kernel(
         const __amdgpu_buffer_rsrc_t dst = rsrc(window + s * g.slot_bytes, g.tail_end);
         if (v < nvec) store16(r, dst, v << 4);
         if (tail_lane) store_tail(dst, g, lane, 0u, src_rank, t, k);
+    }
+}
+
+// Deduplicated bf16 pack: one row per (token, destination rank) instead of per (token, k)
+// ("Ascend DeepEP MoE Dispatch Optimization", section "一条 token 如何走完 MoE": the row is copied once
+// to every rank that holds one of the token's experts). rank_row_idx[t, k] names the row of the
+// rank of expert k (equal for every k of the token on that rank), so only the first k with a given
+// row stores. Row format as the K-fold slot, with the triple (src_rank, t, destination rank).
+// grid = S * nparts; workgroup (t, q) as in pack_bf16_kernel. The token's K rows (and, for the
+// tail lanes, its K ids) are loaded up front into registers: KMAX >= K.
+template <int KMAX>
+__global__ __launch_bounds__(kPartThreads) void pack_dedup_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ rank_row_idx,
+    const int32_t *__restrict__ topk, int K, int E, int epr, int nvec, int nparts, SlotGeom g,
+    int src_rank, int64_t max_rows, uint8_t *__restrict__ window) {
+    const int t = blockIdx.x / nparts;
+    const int q = blockIdx.x - t * nparts;
+    const int lane = threadIdx.x;
+    const int v = q * kPartThreads + lane;
+    const int row_bytes = nvec << 4;
+    int64_t j[KMAX];
+    int e[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        j[k] = k < K ? rank_row_idx[(int64_t)t * K + k] : -1;
+        e[k] = k < K ? topk[(int64_t)t * K + k] : -1;
+    }
+    const u32x4 r = load16(rsrc(x + (int64_t)t * row_bytes, row_bytes), v << 4);
+    const bool tail_lane = q == nparts - 1 && lane < ((g.tail_end - g.payload_bytes) >> 4);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        bool store = j[k] >= 0 && j[k] < max_rows;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) store = store && j[k2] != j[k];  // first k of this rank
+        if (store) {
+            const __amdgpu_buffer_rsrc_t dst = rsrc(window + j[k] * g.slot_bytes, g.tail_end);
+            if (v < nvec) store16(r, dst, v << 4);
+            if (tail_lane)
+                store_tail(dst, g, lane, 0u, src_rank, t, (e[k] >= 0 && e[k] < E) ? e[k] / epr : -1);
+        }
     }
 }
 
@@ -202,6 +244,29 @@ hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_
                                                     max_slots, wb, stream);
     return launch_quant<MOE_QUANT_INT8_DYN>(xb, slot_idx, S, K, ngroups, g, src_rank, max_slots,
                                             wb, stream);
+}
+
+template <int KMAX>
+hipError_t launch_dedup_k(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
+                          int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t src_rank,
+                          void *window, hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
+    const int64_t max_rows = (int64_t)S * (K < P ? K : P);
+    const int nvec = H / 8;
+    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+    hipLaunchKernelGGL((pack_dedup_kernel<KMAX>), dim3((uint32_t)S * nparts), dim3(kPartThreads), 0,
+                       stream, static_cast<const uint8_t *>(x), rank_row_idx, topk_idx, K, E, E / P,
+                       nvec, nparts, g, src_rank, max_rows, static_cast<uint8_t *>(window));
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
+                             int32_t S, int32_t H, int32_t K, int32_t E, int32_t P,
+                             int32_t src_rank, void *window, hipStream_t stream) {
+    if (K <= 2) return launch_dedup_k<2>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
+    if (K <= 4) return launch_dedup_k<4>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
+    if (K <= 8) return launch_dedup_k<8>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
+    return launch_dedup_k<16>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
 }
 
 }  // namespace moe

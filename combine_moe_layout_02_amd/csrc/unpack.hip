@@ -161,7 +161,72 @@ __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
     }
 }
 
+// Receive-side expansion of the deduplicated rows ("Ascend DeepEP MoE Dispatch Optimization",
+// section "一条 token 如何走完 MoE": the destination rank rearranges the rows it received into
+// contiguous per-local-expert input). For every valid (t, k) the row rank_row_idx[t, k] (token t on
+// the rank of expert k) goes to expert-major row slot_idx[t, k] with the triple (src_rank, t, k):
+// the same output the K-fold window's unpack gives. Two launches, output-major so that the rows
+// are written in order: expand_index_kernel writes (t, k) into fields 1-2 of expand_idx[s] for
+// every valid entry; expand_rows_kernel (one workgroup per (output row, part)) then reads them,
+// copies its part of row rank_row_idx[t, k] and fills field 0 with the row's source rank. An
+// expert's rows list its tokens in ascending order, as does a rank's segment, so the reads sweep
+// each segment in order.
+__global__ __launch_bounds__(256) void expand_index_kernel(const int32_t *__restrict__ slot_idx,
+                                                           int K, int64_t n_entries,
+                                                           int64_t max_slots,
+                                                           int32_t *__restrict__ expand_idx) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_entries) return;
+    const int64_t s = slot_idx[i];
+    if (s < 0 || s >= max_slots) return;
+    expand_idx[s * 3 + 1] = (int32_t)(i / K);
+    expand_idx[s * 3 + 2] = (int32_t)(i % K);
+}
+
+__global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
+    const uint8_t *__restrict__ window, const int32_t *__restrict__ rank_row_idx,
+    const int32_t *__restrict__ num_slots, int S, int K, int64_t max_rows, int64_t max_slots,
+    int nparts, SlotGeom g, uint8_t *__restrict__ expand_x, int32_t *__restrict__ expand_idx) {
+    const int64_t s = blockIdx.x / nparts;
+    const int q = blockIdx.x - (int)(s * nparts);
+    const int lane = threadIdx.x;
+    const int v = q * kPartThreads + lane;
+    const int64_t n = min((int64_t)*num_slots, max_slots);
+    if (s >= n) return;
+    const int t = expand_idx[s * 3 + 1], k = expand_idx[s * 3 + 2];
+    if (t < 0 || t >= S || k < 0 || k >= K) return;
+    const int64_t j = rank_row_idx[(int64_t)t * K + k];
+    if (j < 0 || j >= max_rows) return;
+    const __amdgpu_buffer_rsrc_t src = rsrc(window + j * g.slot_bytes, g.tail_end);
+    if ((v << 4) < g.payload_bytes) {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(src, v << 4, 0, kLoadPolicy);
+        const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + s * g.payload_bytes, g.payload_bytes);
+        __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
+    }
+    if (q == nparts - 1 && lane == 0)
+        expand_idx[s * 3] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(src, g.triple_off, 0, kLoadPolicy);
+}
+
 }  // namespace
+
+hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
+                               const int32_t *slot_idx, const int32_t *num_slots, int32_t S,
+                               int32_t K, int32_t P, int32_t H, void *expand_x,
+                               int32_t *expand_idx, hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
+    const int64_t n_entries = (int64_t)S * K;
+    hipLaunchKernelGGL(expand_index_kernel, dim3((uint32_t)((n_entries + 255) / 256)), dim3(256), 0,
+                       stream, slot_idx, K, n_entries, n_entries, expand_idx);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nvec = g.payload_bytes / 16;
+    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+    hipLaunchKernelGGL(expand_rows_kernel, dim3((uint32_t)(n_entries * nparts)), dim3(kPartThreads),
+                       0, stream, static_cast<const uint8_t *>(window), rank_row_idx, num_slots, S,
+                       K, (int64_t)S * (K < P ? K : P), n_entries, nparts, g,
+                       static_cast<uint8_t *>(expand_x), expand_idx);
+    return hipGetLastError();
+}
 
 hipError_t launch_unpack_padded(const void *window, const int32_t *expert_slot_base, int32_t E,
                                 int32_t S, int32_t K, int32_t H, int32_t quant,

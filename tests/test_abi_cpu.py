@@ -232,3 +232,56 @@ def staged_call(stg=A, sstride=14336, slot=A, w=A, S=64, H=7168, K=8, y=A):
 ])
 def test_combine_staged_validation(kw, err):
     assert staged_call(**kw) == err
+
+
+def test_dedup_window_bytes():
+    assert moe.moe_dedup_window_bytes(4096, 8, 8, 7168) == 4096 * 8 * 14848
+    assert moe.moe_dedup_window_bytes(128, 8, 4, 7168) == 128 * 4 * 14848
+    assert moe._lib.moe_dedup_window_bytes(16, 8, 0, 7168) == moe.MOE_ERR_ARG
+    assert moe._lib.moe_dedup_window_bytes(16, 8, 4, 1000) == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(topk=NULL), moe.MOE_ERR_ARG),
+    (dict(E=250, P=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(C=0), moe.MOE_ERR_ARG),
+    (dict(C=65), moe.MOE_ERR_ARG),
+    (dict(K=0), moe.MOE_ERR_ARG),
+    (dict(out=A + 2), moe.MOE_ERR_ALIGN),
+])
+def test_rank_rows_validation(kw, err):
+    a = dict(topk=A, S=64, K=8, E=256, P=8, C=16, out=A)
+    a.update(kw)
+    assert moe._lib.moe_rank_rows(a["topk"], a["S"], a["K"], a["E"], a["P"], a["C"], A, A, a["out"], A,
+                                  None) == err
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(x=NULL), moe.MOE_ERR_ARG),
+    (dict(P=0), moe.MOE_ERR_ARG),
+    (dict(E=12, P=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
+    (dict(x=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(win=A + 256), moe.MOE_ERR_ALIGN),
+    (dict(nbytes=64 * 8 * 14848 - 1), moe.MOE_ERR_WINDOW),
+])
+def test_dispatch_dedup_validation(kw, err):
+    a = dict(x=A, S=64, H=7168, K=8, E=256, P=8, win=A, nbytes=64 * 8 * 14848)
+    a.update(kw)
+    assert moe._lib.moe_dispatch_dedup(a["x"], A, A, a["S"], a["H"], a["K"], a["E"], a["P"], 0, a["win"],
+                                       a["nbytes"], None) == err
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(rr=NULL), moe.MOE_ERR_ARG),
+    (dict(num=NULL), moe.MOE_ERR_ARG),
+    (dict(P=0), moe.MOE_ERR_ARG),
+    (dict(num=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(ex=A + 4), moe.MOE_ERR_ALIGN),
+    (dict(nbytes=100), moe.MOE_ERR_WINDOW),
+])
+def test_expand_dedup_validation(kw, err):
+    a = dict(rr=A, num=A, S=64, K=8, P=8, H=7168, ex=A, nbytes=64 * 8 * 14848)
+    a.update(kw)
+    assert moe._lib.moe_expand_dedup(A, a["nbytes"], a["rr"], A, a["num"], a["S"], a["K"], a["P"], a["H"],
+                                     a["ex"], A, None) == err

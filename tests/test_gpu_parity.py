@@ -387,6 +387,101 @@ def test_unpack_padded_tiny_and_degenerate(moe):
     assert np.all(got[2] == -1) and not got[0].any() and np.all(got[3] == 0) and got[4][0] == 0
 
 
+# ---------------------------------------------------------------- per-rank deduplicated dispatch
+
+
+def gpu_rank_rows(moe, idx, E, P, C):
+    t = to_dev(idx)
+    lay = moe.moe_layout(t, E, P, C)
+    S, K = idx.shape
+    out = moe.RankRows(torch.full((S, K), -7, dtype=torch.int32, device=DEV),
+                       torch.full((P + 1,), -7, dtype=torch.int32, device=DEV))
+    moe.moe_rank_rows(t, lay, E, P, C, out=out)
+    torch.cuda.synchronize()
+    return lay, out
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_rank_rows_workloads(moe, cfg, layout_path):
+    w = WORKLOADS[cfg]
+    idx = inputs(cfg)["topk_idx"]
+    ref_rr, ref_base = oracle.rank_rows(idx, w.E, w.P)
+    for C in sorted({w.C, 1, 3}):
+        note(f"rank_rows cfg{cfg} C={C} path={layout_path}")
+        _, out = gpu_rank_rows(moe, idx, w.E, w.P, C)
+        assert np.array_equal(out.rank_row_idx.cpu().numpy(), ref_rr), C
+        assert np.array_equal(out.rank_token_base.cpu().numpy(), ref_base), C
+
+
+@pytest.mark.parametrize("case", TINY_LAYOUTS)
+def test_rank_rows_tiny(moe, case):
+    S, K, E, P, C, p_mask, p_bad, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
+    note(f"rank_rows tiny {case}")
+    _, out = gpu_rank_rows(moe, idx, E, P, C)
+    ref_rr, ref_base = oracle.rank_rows(idx, E, P)
+    assert np.array_equal(out.rank_row_idx.cpu().numpy(), ref_rr)
+    assert np.array_equal(out.rank_token_base.cpu().numpy(), ref_base)
+
+
+def dedup_dispatch(moe, x_bits, idx, E, P, C, H):
+    S, K = idx.shape
+    t = to_dev(idx)
+    lay, rr = gpu_rank_rows(moe, idx, E, P, C)
+    win = torch.full((moe.moe_dedup_window_bytes(S, K, P, H),), POISON, dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch_dedup(bf16_dev(x_bits), rr.rank_row_idx, t, E, P, win, src_rank=5)
+    torch.cuda.synchronize()
+    return lay, rr, win
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_dispatch_dedup_workloads(moe, cfg):
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    note(f"dispatch_dedup cfg{cfg} {w.describe()}")
+    lay, rr, win = dedup_dispatch(moe, inp["x"], inp["topk_idx"], w.E, w.P, w.C, w.H)
+    ref_rr, _ = oracle.rank_rows(inp["topk_idx"], w.E, w.P)
+    ref = oracle.dispatch_dedup(inp["x"], ref_rr, inp["topk_idx"], w.E, w.P, src_rank=5)
+    geo = oracle.slot_geometry(w.H, 0)
+    m = ref.shape[0]
+    rows = win.view(-1, geo.slot_bytes).cpu().numpy()
+    assert np.array_equal(rows[:m, : geo.tail_end], ref)
+    assert np.all(rows[m:] == POISON)  # rows past M untouched
+    # expansion to expert-major rows equals the K-fold unpack
+    ex, idx = moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H)
+    torch.cuda.synchronize()
+    rex, ridx, _ = oracle.unpack(oracle.dispatch_slots(inp["x"], lay.slot_idx.cpu().numpy(), 0, 5), w.H, 0)
+    n = rex.shape[0]
+    assert np.array_equal(ex.view(torch.uint8).cpu().numpy()[:n], rex)
+    assert np.array_equal(idx.cpu().numpy()[:n], ridx)
+
+
+def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
+    rng = np.random.default_rng(61)
+    for S, K, E, P, C, H in ((45, 6, 12, 4, 5, 32), (17, 16, 32, 32, 17, 64), (100, 3, 8, 1, 7, 48)):
+        tab = random_tiny_routing(rng, S, K, E, p_mask=0.3, p_bad=0.05)
+        x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+        note(f"dedup tiny S={S} K={K} E={E} P={P} C={C} H={H}")
+        lay, rr, win = dedup_dispatch(moe, x, tab, E, P, C, H)
+        ref_rr, _ = oracle.rank_rows(tab, E, P)
+        assert np.array_equal(rr.rank_row_idx.cpu().numpy(), ref_rr)
+        geo = oracle.slot_geometry(H, 0)
+        if (ref_rr >= 0).any():
+            ref = oracle.dispatch_dedup(x, ref_rr, tab, E, P, src_rank=5)
+            rows = win.view(-1, geo.slot_bytes).cpu().numpy()
+            assert np.array_equal(rows[: ref.shape[0], : geo.tail_end], ref)
+        ex = torch.full((S * K, H), -3, dtype=torch.int16, device=DEV)
+        idx = torch.full((S * K, 3), -3, dtype=torch.int32, device=DEV)
+        moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[E:], P, H, out=(ex, idx))
+        torch.cuda.synchronize()
+        rex, ridx, _ = oracle.unpack(oracle.dispatch_slots(x, lay.slot_idx.cpu().numpy(), 0, 5), H, 0)
+        n = rex.shape[0]
+        assert np.array_equal(ex.cpu().numpy().view(np.uint8)[:n], rex)
+        assert np.array_equal(idx.cpu().numpy()[:n], ridx)
+        assert np.all(idx.cpu().numpy()[n:] == -3)
+
+
 # ---------------------------------------------------------------- combine
 
 
