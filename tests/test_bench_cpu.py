@@ -1,0 +1,39 @@
+"""bench.py's byte accounting against the per-workload figures worked out from the definitions
+(algorithmic bytes: what the method must move, no zero padding), and its one-GPU guard. CPU only."""
+
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from conftest import ROOT
+from workloads import WORKLOADS
+
+# (layout, pack, combine) bytes per launch with every entry valid (N = S*K) and C = min(S, 128)
+EXPECTED = {
+    1: (12_968, 790_528, 788_480),
+    2: (224_264, 16_531_456, 16_523_264),
+    3: (432_200, 529_006_592, 528_744_448),
+    4: (432_200, 294_256_640, 528_744_448),
+    5: (1_772_552, 1_058_013_184, 1_057_488_896),
+}
+
+
+@pytest.mark.parametrize("cfg", sorted(EXPECTED))
+def test_algorithmic_bytes(cfg):
+    w = WORKLOADS[cfg]
+    got = bench.algorithmic_bytes(w, w.C, w.S * w.K)
+    assert (got["layout"], got["dispatch"], got["combine"]) == EXPECTED[cfg]
+
+
+def test_per_token_bytes_at_h7168():
+    w = WORKLOADS[3]
+    b = bench.algorithmic_bytes(w, w.C, w.S * w.K)
+    assert b["dispatch"] == 129_152 * w.S and b["combine"] == 129_088 * w.S
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
