@@ -636,6 +636,26 @@ def test_repeat_runs_are_byte_identical(moe):
     assert np.array_equal(y0, y1)
 
 
+def test_maximum_tokens_and_channels(moe):
+    """S = MOE_MAX_TOKENS (65536) with C = MOE_MAX_CHANNELS (4096): layout, dispatch and combine
+    against the oracle on a small hidden size."""
+    rng = np.random.default_rng(77)
+    S, K, H, E, P, C = 65536, 2, 16, 64, 8, 4096
+    idx = random_tiny_routing(rng, S, K, E, p_mask=0.05)
+    note(f"max tokens S={S} K={K} H={H} E={E} P={P} C={C}")
+    got = gpu_layout(moe, idx, E, P, C)
+    ref = oracle.layout(idx, E, P, C)
+    assert_layout_equal(got, ref, "max tokens")
+    x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    win = gpu_dispatch(moe, x, ref["slot_idx"], 0)
+    assert_window_equal(win, oracle.dispatch_slots(x, ref["slot_idx"], 0, 0), oracle.slot_geometry(H, 0),
+                        "max tokens")
+    rows = f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))
+    wts = rng.random((S, K)).astype(np.float32)
+    y = gpu_combine(moe, rows, ref["slot_idx"], wts)
+    assert np.array_equal(y, oracle.combine(rows, ref["slot_idx"], wts))
+
+
 def test_python_layer_rejects_bad_window(moe):
     x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
     slot = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
