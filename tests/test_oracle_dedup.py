@@ -71,9 +71,9 @@ def test_expansion_equals_kfold_unpack(cfg):
     rr, base = rank_rows(inp["topk_idx"], w.E, w.P)
     reg = dispatch_dedup(inp["x"], rr, inp["topk_idx"], w.E, w.P, src_rank=1)
     assert reg.shape[0] == int(base[-1]) == int(lay["num_tokens_per_rank"].sum())
-    ex, idx = expand_dedup(reg, inp["topk_idx"], lay["slot_idx"], w.E, w.P, w.H)
+    ex, idx, sc = expand_dedup(reg, inp["topk_idx"], lay["slot_idx"], w.E, w.P, w.H)
     rex, ridx, _ = unpack(dispatch_slots(inp["x"], lay["slot_idx"], 0, 1), w.H, 0)
-    assert np.array_equal(ex, rex) and np.array_equal(idx, ridx)
+    assert sc is None and np.array_equal(ex, rex) and np.array_equal(idx, ridx)
     if cfg == 3:  # about 5.3 unique ranks per token instead of 8 copies
         assert 5.0 < reg.shape[0] / w.S < 5.6
 
@@ -85,6 +85,10 @@ def test_expansion_with_masks_and_duplicates():
     x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
     lay = layout(tab, E, P, 5)
     rr, _ = rank_rows(tab, E, P)
-    ex, idx = expand_dedup(dispatch_dedup(x, rr, tab, E, P), tab, lay["slot_idx"], E, P, H)
-    rex, ridx, _ = unpack(dispatch_slots(x, lay["slot_idx"], 0, 0), H, 0)
-    assert np.array_equal(ex, rex) and np.array_equal(idx, ridx)
+    for quant in (0, 1, 2):
+        ex, idx, sc = expand_dedup(dispatch_dedup(x, rr, tab, E, P, quant=quant), tab, lay["slot_idx"], E, P,
+                                   H, quant)
+        rex, ridx, rsc = unpack(dispatch_slots(x, lay["slot_idx"], quant, 0), H, quant)
+        assert np.array_equal(ex, rex) and np.array_equal(idx, ridx), quant
+        if quant:
+            assert np.array_equal(sc.view(np.uint32), rsc.view(np.uint32))
