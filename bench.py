@@ -216,7 +216,8 @@ def time_dedup(moe, torch, w, C, lay, window, inputs, n_valid, kfold_pack_bytes,
     x, topk, wts, eo = inputs
     moe.moe_layout(topk, w.E, w.P, C, out=lay)
     rr = moe.moe_rank_rows(topk, lay, w.E, w.P, C)
-    exp = moe.moe_expand_dedup(window, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H)
+    exp = moe.moe_expand_dedup(window, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H,
+                               w.quant)
     torch.cuda.synchronize()
     m = int(rr.rank_token_base[w.P].item())
     ms = {"rank_rows": [], "dispatch_dedup": [], "expand_dedup": []}
@@ -225,16 +226,16 @@ def time_dedup(moe, torch, w, C, lay, window, inputs, n_valid, kfold_pack_bytes,
         e[0].record(stream)
         moe.moe_rank_rows(topk, lay, w.E, w.P, C, out=rr)
         e[1].record(stream)
-        moe.moe_dispatch_dedup(x, rr.rank_row_idx, topk, w.E, w.P, window)
+        moe.moe_dispatch_dedup(x, rr.rank_row_idx, topk, w.E, w.P, window, w.quant)
         e[2].record(stream)
         moe.moe_expand_dedup(window, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H,
-                             out=exp)
+                             w.quant, out=exp)
         e[3].record(stream)
         torch.cuda.synchronize()
         if i >= 3:
             for j, k in enumerate(ms):
                 ms[k].append(e[j].elapsed_time(e[j + 1]))
-    row = 2 * w.H + 12
+    row = (2 * w.H + 12) if w.quant == 0 else (w.H + 16)
     pack_bytes = 2 * w.S * w.H + 8 * w.S * w.K + m * row
     expand_bytes = m * row + n_valid * row + 4 * w.S * w.K + 8 * n_valid + 4
     out = {"rows": m, "rows_per_token": round(m / w.S, 3),
@@ -429,9 +430,8 @@ def main():
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],
                                                                   n_valid, nbytes["combine"], stream)
-        if w.quant == 0:
-            out["extras"]["dedup_dispatch"] = time_dedup(moe, torch, w, C, lay, window, sets[0], n_valid,
-                                                         nbytes["dispatch"], stream)
+        out["extras"]["dedup_dispatch"] = time_dedup(moe, torch, w, C, lay, window, sets[0], n_valid,
+                                                     nbytes["dispatch"], stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, C, inp, eo_host, n_valid)
     print(json.dumps(out), flush=True)

@@ -60,8 +60,8 @@ def _load():
         "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
         "moe_dedup_window_bytes": (I64, [I32, I32, I32, I32]),
         "moe_rank_rows": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P]),
-        "moe_dispatch_dedup": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P]),
-        "moe_expand_dedup": (ctypes.c_int, [P, I64, P, P, P, I32, I32, I32, I32, P, P, P]),
+        "moe_dispatch_dedup": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]),
+        "moe_expand_dedup": (ctypes.c_int, [P, I64, P, P, P, I32, I32, I32, I32, I32, P, P, P, P]),
         "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
                                              P, P, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -316,9 +316,10 @@ def moe_rank_rows(topk_idx, layout, num_experts, num_ranks, num_channels, out=No
     return out
 
 
-def moe_dispatch_dedup(x, rank_row_idx, topk_idx, num_experts, num_ranks, window, src_rank=0,
-                       stream=None):
-    """One bf16 row per (token, destination rank) into the rows named by rank_row_idx."""
+def moe_dispatch_dedup(x, rank_row_idx, topk_idx, num_experts, num_ranks, window, quant=MOE_QUANT_NONE,
+                       src_rank=0, stream=None):
+    """One row per (token, destination rank) into the rows named by rank_row_idx (bf16, or the
+    token's dynamic fp8 / INT8 codes and scale)."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     _need(rank_row_idx, "rank_row_idx", torch.int32, 2, dev)
@@ -330,36 +331,48 @@ def moe_dispatch_dedup(x, rank_row_idx, topk_idx, num_experts, num_ranks, window
         raise ValueError("rank_row_idx and topk_idx must be [S, K] with S rows of x")
     nbytes = window.numel() * window.element_size()
     _check(_lib.moe_dispatch_dedup(_ptr(x), _ptr(rank_row_idx), _ptr(topk_idx), S, H, K,
-                                   int(num_experts), int(num_ranks), int(src_rank), _ptr(window),
-                                   nbytes, _stream(dev, stream)))
+                                   int(num_experts), int(num_ranks), int(quant), int(src_rank),
+                                   _ptr(window), nbytes, _stream(dev, stream)))
     return window
 
 
-def moe_expand_dedup(window, rank_row_idx, slot_idx, num_slots, num_ranks, H, out=None, stream=None):
+def moe_expand_dedup(window, rank_row_idx, slot_idx, num_slots, num_ranks, H, quant=MOE_QUANT_NONE,
+                     out=None, stream=None):
     """Receive-side expansion of the deduplicated rows to the expert-major rows of slot_idx:
-    returns (expand_x bf16 [S*K, H], expand_idx int32 [S*K, 3]) as moe_unpack would. num_slots
-    is the device count N (layout.expert_slot_base[E:])."""
+    returns Unpacked(expand_x [S*K, H] bf16 or uint8 codes, expand_scales fp32 [S*K] or None,
+    expand_idx int32 [S*K, 3]) as moe_unpack would. num_slots is the device count N
+    (layout.expert_slot_base[E:])."""
     _need(window, "window")
     dev = window.device
     _need(rank_row_idx, "rank_row_idx", torch.int32, 2, dev)
     _need(slot_idx, "slot_idx", torch.int32, 2, dev)
     _need(num_slots, "num_slots", torch.int32, device=dev)
     S, K = slot_idx.shape
-    H = int(H)
+    H, quant = int(H), int(quant)
+    rows = S * K
     if tuple(rank_row_idx.shape) != (S, K):
         raise ValueError("rank_row_idx must match slot_idx")
     if out is None:
-        out = (torch.empty((S * K, H), dtype=torch.bfloat16, device=dev),
-               torch.empty((S * K, 3), dtype=torch.int32, device=dev))
-    ex, idx = out
+        if quant == MOE_QUANT_NONE:
+            ex, sc = torch.empty((rows, H), dtype=torch.bfloat16, device=dev), None
+        else:
+            ex = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty(rows, dtype=torch.float32, device=dev)
+        out = Unpacked(ex, sc, torch.empty((rows, 3), dtype=torch.int32, device=dev))
+    ex, sc, idx = out
     _need(ex, "expand_x", device=dev)
     _need(idx, "expand_idx", torch.int32, 2, dev)
-    if ex.numel() * ex.element_size() < S * K * 2 * H or tuple(idx.shape) != (S * K, 3):
-        raise ValueError("expand_x must hold S*K rows of 2H bytes and expand_idx [S*K, 3]")
+    payload = moe_slot_offsets(H, quant)["payload_bytes"]
+    if ex.numel() * ex.element_size() < rows * payload or tuple(idx.shape) != (rows, 3):
+        raise ValueError("expand_x must hold S*K rows of payload bytes and expand_idx [S*K, 3]")
+    if sc is not None:
+        _need(sc, "expand_scales", torch.float32, device=dev)
+        if sc.numel() < rows:
+            raise ValueError("expand_scales must hold S*K values")
     nbytes = window.numel() * window.element_size()
     _check(_lib.moe_expand_dedup(_ptr(window), nbytes, _ptr(rank_row_idx), _ptr(slot_idx),
-                                 _ptr(num_slots), S, K, int(num_ranks), H, _ptr(ex), _ptr(idx),
-                                 _stream(dev, stream)))
+                                 _ptr(num_slots), S, K, int(num_ranks), H, quant, _ptr(ex),
+                                 None if sc is None else _ptr(sc), _ptr(idx), _stream(dev, stream)))
     return out
 
 

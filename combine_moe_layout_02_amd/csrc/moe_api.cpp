@@ -185,8 +185,8 @@ int moe_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int3
 }
 
 int moe_dispatch_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
-                       int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t src_rank,
-                       void *window, int64_t window_bytes, hipStream_t stream) {
+                       int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t quant,
+                       int32_t src_rank, void *window, int64_t window_bytes, hipStream_t stream) {
     if (!x || !rank_row_idx || !topk_idx || !window) return MOE_ERR_ARG;
     int st = check_tokens(S, K);
     if (st != MOE_OK) return st;
@@ -194,17 +194,18 @@ int moe_dispatch_dedup(const void *x, const int32_t *rank_row_idx, const int32_t
     if (st != MOE_OK) return st;
     st = check_experts(E, P);
     if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
     if (!aligned(x, 16) || !aligned(window, 512) || !aligned(rank_row_idx, 4) || !aligned(topk_idx, 4))
         return MOE_ERR_ALIGN;
     if (window_bytes < moe_dedup_window_bytes(S, K, P, H)) return MOE_ERR_WINDOW;
-    return from_hip(moe::launch_pack_dedup(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank,
-                                           window, stream));
+    return from_hip(moe::launch_pack_dedup(x, rank_row_idx, topk_idx, S, H, K, E, P, quant,
+                                           src_rank, window, stream));
 }
 
 int moe_expand_dedup(const void *window, int64_t window_bytes, const int32_t *rank_row_idx,
                      const int32_t *slot_idx, const int32_t *num_slots, int32_t S, int32_t K,
-                     int32_t P, int32_t H, void *expand_x, int32_t *expand_idx,
-                     hipStream_t stream) {
+                     int32_t P, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
+                     int32_t *expand_idx, hipStream_t stream) {
     if (!window || !rank_row_idx || !slot_idx || !num_slots || !expand_x || !expand_idx)
         return MOE_ERR_ARG;
     int st = check_tokens(S, K);
@@ -212,12 +213,15 @@ int moe_expand_dedup(const void *window, int64_t window_bytes, const int32_t *ra
     st = check_hidden(H);
     if (st != MOE_OK) return st;
     if (P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    if (quant != MOE_QUANT_NONE && !expand_scales) return MOE_ERR_ARG;
     if (!aligned(window, 512) || !aligned(expand_x, 16) || !aligned(rank_row_idx, 4) ||
-        !aligned(slot_idx, 4) || !aligned(num_slots, 4) || !aligned(expand_idx, 4))
+        !aligned(slot_idx, 4) || !aligned(num_slots, 4) || !aligned(expand_idx, 4) ||
+        (expand_scales && !aligned(expand_scales, 4)))
         return MOE_ERR_ALIGN;
     if (window_bytes < moe_dedup_window_bytes(S, K, P, H)) return MOE_ERR_WINDOW;
     return from_hip(moe::launch_expand_dedup(window, rank_row_idx, slot_idx, num_slots, S, K, P, H,
-                                             expand_x, expand_idx, stream));
+                                             quant, expand_x, expand_scales, expand_idx, stream));
 }
 
 int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slots, int32_t S,

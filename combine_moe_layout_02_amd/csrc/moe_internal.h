@@ -63,13 +63,13 @@ hipError_t launch_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32
                             int32_t *rank_token_base, hipStream_t stream);
 
 hipError_t launch_pack_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
-                             int32_t S, int32_t H, int32_t K, int32_t E, int32_t P,
+                             int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t quant,
                              int32_t src_rank, void *window, hipStream_t stream);
 
 hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
                                const int32_t *slot_idx, const int32_t *num_slots, int32_t S,
-                               int32_t K, int32_t P, int32_t H, void *expand_x,
-                               int32_t *expand_idx, hipStream_t stream);
+                               int32_t K, int32_t P, int32_t H, int32_t quant, void *expand_x,
+                               float *expand_scales, int32_t *expand_idx, hipStream_t stream);
 
 hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                        int32_t quant, int32_t src_rank, void *window, hipStream_t stream);

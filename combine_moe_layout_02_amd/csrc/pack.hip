@@ -169,15 +169,13 @@ __device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
            (code_of<QUANT>(bf16_lo(w1) / scale) << 16) | (code_of<QUANT>(bf16_hi(w1) / scale) << 24);
 }
 
-// grid = S; workgroup t quantises x[t]. Lane u owns elements [16u, 16u + 16): two input vectors,
-// one 16-byte output vector of codes. blockDim.x = ngroups rounded up to whole waves (at most
-// 1024): on MI355X a workgroup with no idle wave is about 3% faster than a fixed 512 lanes.
+// Quantises row t of x in one workgroup (blockDim.x >= ngroups, whole waves): lane u gets the 16
+// codes of elements [16u, 16u + 16) (zero past the row) and every lane the row's fp32 scale. The
+// row max is a wave shuffle reduction followed by an LDS reduction across waves (wave_max holds
+// one value per wave); scale = amax / top by IEEE division, codes from per-element IEEE divisions.
 template <int QUANT>
-__global__ __launch_bounds__(1024) void pack_quant_kernel(
-    const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int ngroups,
-    SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
-    __shared__ float wave_max[16];
-    const int t = blockIdx.x;
+__device__ inline void quantise_row(const uint8_t *__restrict__ x, int t, int ngroups,
+                                    float *wave_max, u32x4 &codes, uint32_t &scale_bits) {
     const int u = threadIdx.x, lane = u & 63, wave = u >> 6;
     const int row_bytes = ngroups << 5;
     const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
@@ -197,11 +195,26 @@ __global__ __launch_bounds__(1024) void pack_quant_kernel(
     for (int w = 0; w < nwaves; ++w) amax = fmaxf(amax, wave_max[w]);
 
     const float scale = amax / code_max<QUANT>();  // IEEE round-to-nearest division
-    u32x4 codes = {0u, 0u, 0u, 0u};
+    codes = u32x4{0u, 0u, 0u, 0u};
     if (u < ngroups && amax > 0.0f)
         codes = u32x4{quant4<QUANT>(a[0], a[1], scale), quant4<QUANT>(a[2], a[3], scale),
                       quant4<QUANT>(b[0], b[1], scale), quant4<QUANT>(b[2], b[3], scale)};
-    const uint32_t scale_bits = __float_as_uint(scale);
+    scale_bits = __float_as_uint(scale);
+}
+
+// grid = S; workgroup t quantises x[t] and writes the codes to its K slots. blockDim.x = ngroups
+// rounded up to whole waves (at most 1024): on MI355X a workgroup with no idle wave is about 3%
+// faster than a fixed 512 lanes.
+template <int QUANT>
+__global__ __launch_bounds__(1024) void pack_quant_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ slot_idx, int K, int ngroups,
+    SlotGeom g, int src_rank, int64_t max_slots, uint8_t *__restrict__ window) {
+    __shared__ float wave_max[16];
+    const int t = blockIdx.x;
+    const int u = threadIdx.x;
+    u32x4 codes;
+    uint32_t scale_bits;
+    quantise_row<QUANT>(x, t, ngroups, wave_max, codes, scale_bits);
     const bool tail_lane = u < ((g.tail_end - g.payload_bytes) >> 4);
     const int32_t *slots = slot_idx + (int64_t)t * K;
     for (int k = 0; k < K; ++k) {
@@ -210,6 +223,42 @@ __global__ __launch_bounds__(1024) void pack_quant_kernel(
         const __amdgpu_buffer_rsrc_t dst = rsrc(window + s * g.slot_bytes, g.tail_end);
         if (u < ngroups) store16(codes, dst, u << 4);
         if (tail_lane) store_tail(dst, g, u, scale_bits, src_rank, t, k);
+    }
+}
+
+// Deduplicated quantised pack: the codes of row t go once to each destination rank's row (the
+// first k of each rank in rank_row_idx), with the scale and the triple (src_rank, t, rank).
+template <int KMAX, int QUANT>
+__global__ __launch_bounds__(1024) void pack_dedup_quant_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ rank_row_idx,
+    const int32_t *__restrict__ topk, int K, int E, int epr, int ngroups, SlotGeom g, int src_rank,
+    int64_t max_rows, uint8_t *__restrict__ window) {
+    __shared__ float wave_max[16];
+    const int t = blockIdx.x;
+    const int u = threadIdx.x;
+    int64_t j[KMAX];
+    int e[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        j[k] = k < K ? rank_row_idx[(int64_t)t * K + k] : -1;
+        e[k] = k < K ? topk[(int64_t)t * K + k] : -1;
+    }
+    u32x4 codes;
+    uint32_t scale_bits;
+    quantise_row<QUANT>(x, t, ngroups, wave_max, codes, scale_bits);
+    const bool tail_lane = u < ((g.tail_end - g.payload_bytes) >> 4);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        bool store = j[k] >= 0 && j[k] < max_rows;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) store = store && j[k2] != j[k];  // first k of this rank
+        if (store) {
+            const __amdgpu_buffer_rsrc_t dst = rsrc(window + j[k] * g.slot_bytes, g.tail_end);
+            if (u < ngroups) store16(codes, dst, u << 4);
+            if (tail_lane)
+                store_tail(dst, g, u, scale_bits, src_rank, t,
+                           (e[k] >= 0 && e[k] < E) ? e[k] / epr : -1);
+        }
     }
 }
 
@@ -248,25 +297,40 @@ hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_
 
 template <int KMAX>
 hipError_t launch_dedup_k(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
-                          int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t src_rank,
-                          void *window, hipStream_t stream) {
-    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
+                          int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t quant,
+                          int32_t src_rank, void *window, hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, quant);
     const int64_t max_rows = (int64_t)S * (K < P ? K : P);
-    const int nvec = H / 8;
-    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
-    hipLaunchKernelGGL((pack_dedup_kernel<KMAX>), dim3((uint32_t)S * nparts), dim3(kPartThreads), 0,
-                       stream, static_cast<const uint8_t *>(x), rank_row_idx, topk_idx, K, E, E / P,
-                       nvec, nparts, g, src_rank, max_rows, static_cast<uint8_t *>(window));
+    const uint8_t *xb = static_cast<const uint8_t *>(x);
+    uint8_t *wb = static_cast<uint8_t *>(window);
+    if (quant == MOE_QUANT_NONE) {
+        const int nvec = H / 8;
+        const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
+        hipLaunchKernelGGL((pack_dedup_kernel<KMAX>), dim3((uint32_t)S * nparts), dim3(kPartThreads),
+                           0, stream, xb, rank_row_idx, topk_idx, K, E, E / P, nvec, nparts, g,
+                           src_rank, max_rows, wb);
+        return hipGetLastError();
+    }
+    const int ngroups = H / 16;
+    const int threads = (ngroups + 63) & ~63;
+    if (quant == MOE_QUANT_FP8_E4M3_DYN)
+        hipLaunchKernelGGL((pack_dedup_quant_kernel<KMAX, MOE_QUANT_FP8_E4M3_DYN>), dim3(S),
+                           dim3(threads), 0, stream, xb, rank_row_idx, topk_idx, K, E, E / P, ngroups,
+                           g, src_rank, max_rows, wb);
+    else
+        hipLaunchKernelGGL((pack_dedup_quant_kernel<KMAX, MOE_QUANT_INT8_DYN>), dim3(S),
+                           dim3(threads), 0, stream, xb, rank_row_idx, topk_idx, K, E, E / P, ngroups,
+                           g, src_rank, max_rows, wb);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
-                             int32_t S, int32_t H, int32_t K, int32_t E, int32_t P,
+                             int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t quant,
                              int32_t src_rank, void *window, hipStream_t stream) {
-    if (K <= 2) return launch_dedup_k<2>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
-    if (K <= 4) return launch_dedup_k<4>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
-    if (K <= 8) return launch_dedup_k<8>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
-    return launch_dedup_k<16>(x, rank_row_idx, topk_idx, S, H, K, E, P, src_rank, window, stream);
+    if (K <= 2) return launch_dedup_k<2>(x, rank_row_idx, topk_idx, S, H, K, E, P, quant, src_rank, window, stream);
+    if (K <= 4) return launch_dedup_k<4>(x, rank_row_idx, topk_idx, S, H, K, E, P, quant, src_rank, window, stream);
+    if (K <= 8) return launch_dedup_k<8>(x, rank_row_idx, topk_idx, S, H, K, E, P, quant, src_rank, window, stream);
+    return launch_dedup_k<16>(x, rank_row_idx, topk_idx, S, H, K, E, P, quant, src_rank, window, stream);
 }
 
 }  // namespace moe

@@ -168,7 +168,8 @@ __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
 // the same output the K-fold window's unpack gives. Two launches, output-major so that the rows
 // are written in order: expand_index_kernel writes (t, k) into fields 1-2 of expand_idx[s] for
 // every valid entry; expand_rows_kernel (one workgroup per (output row, part)) then reads them,
-// copies its part of row rank_row_idx[t, k] and fills field 0 with the row's source rank. An
+// copies its part of row rank_row_idx[t, k] and fills field 0 with the row's source rank (and, for
+// quantised rows, expand_scales[s] with the row's scale). An
 // expert's rows list its tokens in ascending order, as does a rank's segment, so the reads sweep
 // each segment in order.
 __global__ __launch_bounds__(256) void expand_index_kernel(const int32_t *__restrict__ slot_idx,
@@ -186,7 +187,8 @@ __global__ __launch_bounds__(256) void expand_index_kernel(const int32_t *__rest
 __global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
     const uint8_t *__restrict__ window, const int32_t *__restrict__ rank_row_idx,
     const int32_t *__restrict__ num_slots, int S, int K, int64_t max_rows, int64_t max_slots,
-    int nparts, SlotGeom g, uint8_t *__restrict__ expand_x, int32_t *__restrict__ expand_idx) {
+    int nparts, SlotGeom g, bool quantised, uint8_t *__restrict__ expand_x,
+    float *__restrict__ expand_scales, int32_t *__restrict__ expand_idx) {
     const int64_t s = blockIdx.x / nparts;
     const int q = blockIdx.x - (int)(s * nparts);
     const int lane = threadIdx.x;
@@ -203,17 +205,21 @@ __global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
         const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + s * g.payload_bytes, g.payload_bytes);
         __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
     }
-    if (q == nparts - 1 && lane == 0)
+    if (q == nparts - 1 && lane == 0) {
         expand_idx[s * 3] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(src, g.triple_off, 0, kLoadPolicy);
+        if (quantised)
+            expand_scales[s] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(src, g.scale_off, 0, kLoadPolicy));
+    }
 }
 
 }  // namespace
 
 hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
                                const int32_t *slot_idx, const int32_t *num_slots, int32_t S,
-                               int32_t K, int32_t P, int32_t H, void *expand_x,
-                               int32_t *expand_idx, hipStream_t stream) {
-    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
+                               int32_t K, int32_t P, int32_t H, int32_t quant, void *expand_x,
+                               float *expand_scales, int32_t *expand_idx, hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, quant);
     const int64_t n_entries = (int64_t)S * K;
     hipLaunchKernelGGL(expand_index_kernel, dim3((uint32_t)((n_entries + 255) / 256)), dim3(256), 0,
                        stream, slot_idx, K, n_entries, n_entries, expand_idx);
@@ -224,7 +230,8 @@ hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
     hipLaunchKernelGGL(expand_rows_kernel, dim3((uint32_t)(n_entries * nparts)), dim3(kPartThreads),
                        0, stream, static_cast<const uint8_t *>(window), rank_row_idx, num_slots, S,
                        K, (int64_t)S * (K < P ? K : P), n_entries, nparts, g,
-                       static_cast<uint8_t *>(expand_x), expand_idx);
+                       quant != MOE_QUANT_NONE, static_cast<uint8_t *>(expand_x), expand_scales,
+                       expand_idx);
     return hipGetLastError();
 }
 

@@ -211,7 +211,8 @@ int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slot
  * Optimization", section "一条 token 如何走完 MoE": a token's row is copied once to each rank that holds
  * one of its experts, and the receiving rank rearranges it into per-local-expert input; sections
  * "P 维路由为什么值得单独优化" and "所谓 compact plan 到底压缩了什么": only a token's real destinations
- * are planned, aggregated into one contiguous segment per rank). bf16 payload only.
+ * are planned, aggregated into one contiguous segment per rank). Payloads as for moe_dispatch: bf16,
+ * or per-token dynamic fp8 E4M3 / INT8 codes with the scale in the row's scale block.
  *
  * Rank r's segment starts at rank_token_base[r] (exclusive prefix of num_tokens_per_rank, [P] = M,
  * the number of rows) and lists the tokens with a valid expert on r in ascending token order.
@@ -226,13 +227,16 @@ int moe_unpack(const void *window, int64_t window_bytes, const int32_t *num_slot
  * moe_rank_rows:      in:  topk_idx, S, K, E, P, C as for moe_layout, and its outputs
  *                          rank_prefix_matrix [P, C] and num_tokens_per_rank [P];
  *                     out: rank_row_idx int32 [S, K], rank_token_base int32 [P + 1]. One kernel.
- * moe_dispatch_dedup: in:  x bf16 [S, H] (16-byte aligned), rank_row_idx, topk_idx, E, P,
+ * moe_dispatch_dedup: in:  x bf16 [S, H] (16-byte aligned), rank_row_idx, topk_idx, E, P, quant,
  *                          src_rank; window 512-byte aligned, window_bytes >= moe_dedup_window_bytes;
- *                     writes bytes [0, tail_end) of rows 0..M-1 (see moe_slot_offsets).
+ *                     writes bytes [0, tail_end) of rows 0..M-1 (see moe_slot_offsets), the codes
+ *                     and scale computed exactly as moe_dispatch computes them.
  * moe_expand_dedup:   in:  the deduplicated window; rank_row_idx [S, K] from moe_rank_rows;
  *                          slot_idx [S, K] from moe_layout; num_slots = DEVICE pointer to N, the
- *                          valid-entry count (&expert_slot_base[E]); P;
- *                     out: expand_x [S*K, 2H] bytes (16-byte aligned) and expand_idx int32 [S*K, 3]:
+ *                          valid-entry count (&expert_slot_base[E]); P; quant as dispatched;
+ *                     out: expand_x [S*K, payload_bytes] bytes (16-byte aligned), expand_scales
+ *                          fp32 [S*K] (quantised modes; may be NULL for bf16) and expand_idx int32
+ *                          [S*K, 3]:
  *                          for every valid (t, k), row slot_idx[t, k] gets row rank_row_idx[t, k]
  *                          (token t on the rank of expert k) and the triple (src_rank read from that
  *                          row, t, k), which is exactly what moe_unpack of the K-fold window writes;
@@ -245,13 +249,13 @@ int moe_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int3
                   int32_t *rank_row_idx, int32_t *rank_token_base, hipStream_t stream);
 
 int moe_dispatch_dedup(const void *x, const int32_t *rank_row_idx, const int32_t *topk_idx,
-                       int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t src_rank,
-                       void *window, int64_t window_bytes, hipStream_t stream);
+                       int32_t S, int32_t H, int32_t K, int32_t E, int32_t P, int32_t quant,
+                       int32_t src_rank, void *window, int64_t window_bytes, hipStream_t stream);
 
 int moe_expand_dedup(const void *window, int64_t window_bytes, const int32_t *rank_row_idx,
                      const int32_t *slot_idx, const int32_t *num_slots, int32_t S, int32_t K,
-                     int32_t P, int32_t H, void *expand_x, int32_t *expand_idx,
-                     hipStream_t stream);
+                     int32_t P, int32_t H, int32_t quant, void *expand_x, float *expand_scales,
+                     int32_t *expand_idx, hipStream_t stream);
 
 /* Padded unpack: the rows of moe_unpack placed for a grouped GEMM whose per-expert blocks start on
  * a multiple of expert_alignment, in an output of exactly out_rows rows. Two options of DeepEP's

@@ -140,6 +140,8 @@ def unpack_call(win=A, nbytes=None, num=A, S=64, K=8, H=7168, quant=0, ex=A, sc=
     (dict(win=A + 64), moe.MOE_ERR_ALIGN),
     (dict(ex=A + 8), moe.MOE_ERR_ALIGN),
     (dict(num=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(quant=1, sc=NULL), moe.MOE_ERR_ARG),
+    (dict(quant=-1), moe.MOE_ERR_ARG),
     (dict(nbytes=64 * 8 * 14848 - 512), moe.MOE_ERR_WINDOW),
 ])
 def test_unpack_validation(kw, err):
@@ -263,13 +265,14 @@ def test_rank_rows_validation(kw, err):
     (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
     (dict(x=A + 8), moe.MOE_ERR_ALIGN),
     (dict(win=A + 256), moe.MOE_ERR_ALIGN),
+    (dict(quant=3), moe.MOE_ERR_ARG),
     (dict(nbytes=64 * 8 * 14848 - 1), moe.MOE_ERR_WINDOW),
 ])
 def test_dispatch_dedup_validation(kw, err):
-    a = dict(x=A, S=64, H=7168, K=8, E=256, P=8, win=A, nbytes=64 * 8 * 14848)
+    a = dict(x=A, S=64, H=7168, K=8, E=256, P=8, quant=0, win=A, nbytes=64 * 8 * 14848)
     a.update(kw)
-    assert moe._lib.moe_dispatch_dedup(a["x"], A, A, a["S"], a["H"], a["K"], a["E"], a["P"], 0, a["win"],
-                                       a["nbytes"], None) == err
+    assert moe._lib.moe_dispatch_dedup(a["x"], A, A, a["S"], a["H"], a["K"], a["E"], a["P"], a["quant"], 0,
+                                       a["win"], a["nbytes"], None) == err
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -277,11 +280,13 @@ def test_dispatch_dedup_validation(kw, err):
     (dict(num=NULL), moe.MOE_ERR_ARG),
     (dict(P=0), moe.MOE_ERR_ARG),
     (dict(num=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(quant=1, sc=NULL), moe.MOE_ERR_ARG),
+    (dict(quant=-1), moe.MOE_ERR_ARG),
     (dict(ex=A + 4), moe.MOE_ERR_ALIGN),
     (dict(nbytes=100), moe.MOE_ERR_WINDOW),
 ])
 def test_expand_dedup_validation(kw, err):
-    a = dict(rr=A, num=A, S=64, K=8, P=8, H=7168, ex=A, nbytes=64 * 8 * 14848)
+    a = dict(rr=A, num=A, S=64, K=8, P=8, H=7168, quant=0, ex=A, sc=A, nbytes=64 * 8 * 14848)
     a.update(kw)
     assert moe._lib.moe_expand_dedup(A, a["nbytes"], a["rr"], A, a["num"], a["S"], a["K"], a["P"], a["H"],
-                                     a["ex"], A, None) == err
+                                     a["quant"], a["ex"], a["sc"], A, None) == err

@@ -425,36 +425,48 @@ def test_rank_rows_tiny(moe, case):
     assert np.array_equal(out.rank_token_base.cpu().numpy(), ref_base)
 
 
-def dedup_dispatch(moe, x_bits, idx, E, P, C, H):
+def dedup_dispatch(moe, x_bits, idx, E, P, C, H, quant=0):
     S, K = idx.shape
     t = to_dev(idx)
     lay, rr = gpu_rank_rows(moe, idx, E, P, C)
     win = torch.full((moe.moe_dedup_window_bytes(S, K, P, H),), POISON, dtype=torch.uint8, device=DEV)
-    moe.moe_dispatch_dedup(bf16_dev(x_bits), rr.rank_row_idx, t, E, P, win, src_rank=5)
+    moe.moe_dispatch_dedup(bf16_dev(x_bits), rr.rank_row_idx, t, E, P, win, quant=quant, src_rank=5)
     torch.cuda.synchronize()
     return lay, rr, win
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
-def test_dispatch_dedup_workloads(moe, cfg):
+def check_expansion(moe, win, rr, lay, x_bits, E, P, H, quant, prefill=None):
+    """Expand the dedup rows and compare with the oracle's unpack of the K-fold window."""
+    S, K = lay.slot_idx.shape
+    out = prefill
+    got = moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[E:], P, H, quant,
+                               out=out)
+    torch.cuda.synchronize()
+    rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(x_bits, lay.slot_idx.cpu().numpy(), quant, 5), H, quant)
+    n = rex.shape[0]
+    ex = got.expand_x.view(torch.uint8).cpu().numpy().reshape(S * K, -1)
+    assert np.array_equal(ex[:n], rex)
+    assert np.array_equal(got.expand_idx.cpu().numpy()[:n], ridx)
+    if quant:
+        assert np.array_equal(got.expand_scales.cpu().numpy()[:n].view(np.uint32), rsc.view(np.uint32))
+    return got, n
+
+
+@pytest.mark.parametrize("cfg,quant", [(1, 0), (2, 0), (3, 0), (5, 0), (2, 1), (4, 1), (4, 2)])
+def test_dispatch_dedup_workloads(moe, cfg, quant):
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
-    note(f"dispatch_dedup cfg{cfg} {w.describe()}")
-    lay, rr, win = dedup_dispatch(moe, inp["x"], inp["topk_idx"], w.E, w.P, w.C, w.H)
+    note(f"dispatch_dedup cfg{cfg} quant {quant} {w.describe()}")
+    lay, rr, win = dedup_dispatch(moe, inp["x"], inp["topk_idx"], w.E, w.P, w.C, w.H, quant)
     ref_rr, _ = oracle.rank_rows(inp["topk_idx"], w.E, w.P)
-    ref = oracle.dispatch_dedup(inp["x"], ref_rr, inp["topk_idx"], w.E, w.P, src_rank=5)
-    geo = oracle.slot_geometry(w.H, 0)
+    ref = oracle.dispatch_dedup(inp["x"], ref_rr, inp["topk_idx"], w.E, w.P, src_rank=5, quant=quant)
+    geo = oracle.slot_geometry(w.H, quant)
     m = ref.shape[0]
     rows = win.view(-1, geo.slot_bytes).cpu().numpy()
     assert np.array_equal(rows[:m, : geo.tail_end], ref)
     assert np.all(rows[m:] == POISON)  # rows past M untouched
     # expansion to expert-major rows equals the K-fold unpack
-    ex, idx = moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[w.E:], w.P, w.H)
-    torch.cuda.synchronize()
-    rex, ridx, _ = oracle.unpack(oracle.dispatch_slots(inp["x"], lay.slot_idx.cpu().numpy(), 0, 5), w.H, 0)
-    n = rex.shape[0]
-    assert np.array_equal(ex.view(torch.uint8).cpu().numpy()[:n], rex)
-    assert np.array_equal(idx.cpu().numpy()[:n], ridx)
+    check_expansion(moe, win, rr, lay, inp["x"], w.E, w.P, w.H, quant)
 
 
 def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
@@ -462,24 +474,23 @@ def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
     for S, K, E, P, C, H in ((45, 6, 12, 4, 5, 32), (17, 16, 32, 32, 17, 64), (100, 3, 8, 1, 7, 48)):
         tab = random_tiny_routing(rng, S, K, E, p_mask=0.3, p_bad=0.05)
         x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
-        note(f"dedup tiny S={S} K={K} E={E} P={P} C={C} H={H}")
-        lay, rr, win = dedup_dispatch(moe, x, tab, E, P, C, H)
-        ref_rr, _ = oracle.rank_rows(tab, E, P)
-        assert np.array_equal(rr.rank_row_idx.cpu().numpy(), ref_rr)
-        geo = oracle.slot_geometry(H, 0)
-        if (ref_rr >= 0).any():
-            ref = oracle.dispatch_dedup(x, ref_rr, tab, E, P, src_rank=5)
-            rows = win.view(-1, geo.slot_bytes).cpu().numpy()
-            assert np.array_equal(rows[: ref.shape[0], : geo.tail_end], ref)
-        ex = torch.full((S * K, H), -3, dtype=torch.int16, device=DEV)
-        idx = torch.full((S * K, 3), -3, dtype=torch.int32, device=DEV)
-        moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[E:], P, H, out=(ex, idx))
-        torch.cuda.synchronize()
-        rex, ridx, _ = oracle.unpack(oracle.dispatch_slots(x, lay.slot_idx.cpu().numpy(), 0, 5), H, 0)
-        n = rex.shape[0]
-        assert np.array_equal(ex.cpu().numpy().view(np.uint8)[:n], rex)
-        assert np.array_equal(idx.cpu().numpy()[:n], ridx)
-        assert np.all(idx.cpu().numpy()[n:] == -3)
+        for quant in (0, 1, 2):
+            note(f"dedup tiny S={S} K={K} E={E} P={P} C={C} H={H} quant {quant}")
+            lay, rr, win = dedup_dispatch(moe, x, tab, E, P, C, H, quant)
+            ref_rr, _ = oracle.rank_rows(tab, E, P)
+            assert np.array_equal(rr.rank_row_idx.cpu().numpy(), ref_rr)
+            geo = oracle.slot_geometry(H, quant)
+            if (ref_rr >= 0).any():
+                ref = oracle.dispatch_dedup(x, ref_rr, tab, E, P, src_rank=5, quant=quant)
+                rows = win.view(-1, geo.slot_bytes).cpu().numpy()
+                assert np.array_equal(rows[: ref.shape[0], : geo.tail_end], ref)
+            width = H if quant else 2 * H
+            pre = moe.Unpacked(torch.full((S * K, width), 0xCD, dtype=torch.uint8, device=DEV),
+                               torch.full((S * K,), -2.0, dtype=torch.float32, device=DEV) if quant else None,
+                               torch.full((S * K, 3), -3, dtype=torch.int32, device=DEV))
+            got, n = check_expansion(moe, win, rr, lay, x, E, P, H, quant, prefill=pre)
+            assert np.all(got.expand_idx.cpu().numpy()[n:] == -3)  # rows past N keep their contents
+            assert np.all(got.expand_x.cpu().numpy()[n:] == 0xCD)
 
 
 # ---------------------------------------------------------------- combine
