@@ -1,4 +1,5 @@
-// Dispatch pack kernels for gfx950: K-fold expanded copy of token rows into window slots.
+// Dispatch pack kernels for gfx950: K-fold expanded copy of token rows into window slots, and the
+// per-rank deduplicated copy.
 //
 // The CAM pack ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 InputToShare) walks the
 // (token, k) pairs and re-reads the token row for every copy. Here each row is read from HBM once
@@ -18,6 +19,10 @@
 // row's maximum before any code is known, so one workgroup owns one token: each lane holds 16
 // elements (one 16-byte vector of codes), the row max is a wave shuffle reduction followed by an
 // LDS reduction across waves, then codes are written to the K slots.
+//
+// The deduplicated variants (DeepEP's one copy per destination rank, "Ascend DeepEP MoE Dispatch
+// Optimization", section "一条 token 如何走完 MoE") keep the same workgroup shapes and store each row
+// once per destination rank instead of once per k.
 //
 // Stores use buffer instructions with the sc0 sc1 nt cache policy: the window is written once and
 // not read back by this kernel, so the lines stream to HBM instead of filling L2 and the
