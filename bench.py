@@ -15,6 +15,10 @@ extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
 bounds the event timings at decode sizes.
 
+kernels: event statistics per call (layout, dispatch = the pack, combine) and
+for the sums layout+dispatch and layout+dispatch+combine, each with its bytes,
+GB/s, fraction of 8 TB/s, tokens/s and fraction of the measured copy ceiling.
+
 Algorithmic bytes (what the method must move; zero padding and the window
 reservation are not traffic):
   layout   = topk_idx + is_token_in_rank + counts + slot bases + slot_idx + both prefix matrices
@@ -95,8 +99,20 @@ def cpu_baseline(w, C, inp, expert_out, n_valid, min_seconds=10.0, max_reps=25):
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
         "sample": f"{reps} full steps (layout+dispatch+combine) of {w.describe()}, {wall:.1f} s wall, "
-                  f"{cpu:.1f} s cpu, {reps * w.S / wall:.0f} tokens/s; host has {os.cpu_count()} logical cpus",
+                  f"{cpu:.1f} s cpu, {reps * w.S / wall:.0f} tokens/s; numpy on one thread; host has "
+                  f"{os.cpu_count()} logical cpus ({cpu_model()})",
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "cpu model unknown"
 
 
 def copy_ceiling(torch, dev, mib=1024, iters=10):
@@ -366,14 +382,20 @@ def main():
             ms["layout"].append(e[0].elapsed_time(e[1]))
             ms["dispatch"].append(e[1].elapsed_time(e[2]))
             ms["combine"].append(e[2].elapsed_time(e[3]))
+        ms["layout+dispatch"] = [a + b for a, b in zip(ms["layout"], ms["dispatch"])]
+        ms["layout+dispatch+combine"] = [a + b for a, b in zip(ms["layout+dispatch"], ms["combine"])]
+        nb = dict(nbytes)
+        nb["layout+dispatch"] = nbytes["layout"] + nbytes["dispatch"]
+        nb["layout+dispatch+combine"] = nb["layout+dispatch"] + nbytes["combine"]
         kernels = {}
         for k, v in ms.items():
             avg_us = 1e3 * float(np.mean(v))
-            gbs = nbytes[k] / (avg_us * 1e-6) / 1e9
+            gbs = nb[k] / (avg_us * 1e-6) / 1e9
             kernels[k] = {
                 "avg_us": round(avg_us, 2), "min_us": round(1e3 * float(np.min(v)), 2),
-                "median_us": round(1e3 * float(np.median(v)), 2), "bytes": nbytes[k],
+                "median_us": round(1e3 * float(np.median(v)), 2), "bytes": nb[k],
                 "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(w.S / (avg_us * 1e-6), 1),
             }
             if copy_gbs:
                 kernels[k]["frac_copy_ceiling"] = round(gbs / copy_gbs, 4)
