@@ -63,7 +63,6 @@ constexpr size_t max2(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kLdsBytes =
     max2(max2(sizeof(SlotLds), sizeof(ExpertLds)), max2(sizeof(RankLds), sizeof(TokenLds)));
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup on gfx950");
-static_assert(kMaxWords < 64, "a rank row's word prefix must fit in one wave");
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: row_shr 1, 2, 4, 8 within each row of
 // 16 lanes, then row_bcast:15 and row_bcast:31 carry row totals upward. Lanes with no source lane
@@ -208,10 +207,15 @@ __device__ void ranks_role(RankLds &L, int r0, const int32_t *__restrict__ topk,
     }
     __syncthreads();
     if (wave < rows) {
-        // exclusive popcount prefix over the row's words; lane W holds the row total (W < 64)
-        const int pc = lane < W ? __popcll(L.bits[wave][lane]) : 0;
-        const int incl = wave_inclusive_scan(pc);
-        if (lane <= W) L.pre[wave][lane] = incl - pc;
+        // exclusive popcount prefix over the row's words, 64 words per step; pre[W] is the total
+        int carry = 0;
+        for (int w0 = 0; w0 <= W; w0 += 64) {
+            const int w = w0 + lane;
+            const int pc = w < W ? __popcll(L.bits[wave][w]) : 0;
+            const int incl = wave_inclusive_scan(pc);
+            if (w <= W) L.pre[wave][w] = carry + incl - pc;
+            carry += lane_value(incl, 63);
+        }
         const int per = S / C, rem = S % C;
         int32_t *row = rank_prefix + (int64_t)(r0 + wave) * C;
         for (int c = lane; c < C; c += 64) {
@@ -221,7 +225,7 @@ __device__ void ranks_role(RankLds &L, int r0, const int32_t *__restrict__ topk,
             if (b) val += __popcll(L.bits[wave][w] & ((1ull << b) - 1ull));
             row[c] = val;
         }
-        if (lane == 0) num_tokens_per_rank[r0 + wave] = lane_value(incl, 63);
+        if (lane == 0) num_tokens_per_rank[r0 + wave] = carry;
     }
 }
 

@@ -36,7 +36,7 @@ inline SlotGeom slot_geom(int32_t H, int32_t quant) {
 }
 
 // Limits of the single-launch layout for small routing tables (its LDS tables are sized by them).
-constexpr int kSmallLayoutEntries = 2048;   // S * K
+constexpr int kSmallLayoutEntries = 4096;   // S * K
 constexpr int kSmallLayoutChannels = 1024;  // C
 
 // True when the single-launch layout can take (S, K, E, P, C).

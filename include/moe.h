@@ -103,7 +103,7 @@ int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *
  *                                          slots are the contiguous range
  *                                          [rank_slot_base[r], rank_slot_base[r+1]).
  *      status                int32 [1]     0, or bit 0 set if an id outside [-1, E) was seen
- * Enqueues one kernel on `stream` when S*K <= 2048 and C <= 1024 (decode-sized tables: every
+ * Enqueues one kernel on `stream` when S*K <= 4096 and C <= 1024 (decode-sized tables: every
  * workgroup rereads the table and writes its own share of the outputs), otherwise three kernels
  * (count per channel, scan along channels, assign). Both give identical outputs; setting the
  * environment variable MOE_LAYOUT_SMALL=0 forces the three-kernel form (read on every call).

@@ -155,11 +155,12 @@ TINY_LAYOUTS = [
     (257, 2, 384, 384, 257, 0.0, 0.0, 5),  # P_MAX, one expert per rank, C = S
     (1000, 8, 64, 8, 1, 0.05, 0.0, 6),    # one channel, many chunks
     (600, 6, 5, 5, 600, 0.5, 0.02, 7),    # heavy masking, duplicate-prone
-    (256, 8, 256, 8, 128, 0.0, 0.0, 8),   # S*K = 2048: largest table of the single-launch path
-    (257, 8, 256, 8, 128, 0.0, 0.0, 9),   # one token more: three launches
+    (512, 8, 256, 8, 128, 0.0, 0.0, 8),   # S*K = 4096: largest table of the single-launch path
+    (513, 8, 256, 8, 128, 0.0, 0.0, 9),   # one token more: three launches
+    (4096, 1, 16, 4, 1000, 0.1, 0.0, 14),  # S = 4096: 64 bitset words per rank row
     (64, 8, 512, 256, 64, 0.1, 0.05, 10),  # E at its maximum on the single-launch path
     (64, 4, 384, 384, 64, 0.1, 0.0, 12),  # P at its maximum on the single-launch path
-    (2048, 1, 16, 4, 1024, 0.1, 0.0, 13),  # S*K = 2048 with K = 1, C at its maximum (1024)
+    (2048, 2, 16, 4, 1024, 0.1, 0.0, 13),  # S*K = 4096 with C at its maximum (1024)
     (200, 3, 9, 3, 7, 0.0, 0.0, 11),      # S not a multiple of 64, ragged channels
 ]
 
