@@ -67,5 +67,19 @@ def build(verbose=False, extra_flags=()):
     return LIB
 
 
+def build_abi_harness(verbose=False):
+    """The C++ consumer of the C ABI used by the GPU tests (tests/c_abi/abi_gpu.cpp), linked
+    against libmoe.so; lands next to its source."""
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_gpu.cpp")
+    exe = os.path.join(ROOT, "tests", "c_abi", "abi_gpu")
+    cmd = [hipcc(), "-x", "hip", "-O2", "-std=c++17", f"--offload-arch={ARCH}", f"-I{INCLUDE}", src, "-o",
+           exe, f"-L{PKG}", "-lmoe", f"-Wl,-rpath,{PKG}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _run(cmd)
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_abi_harness(verbose="-v" in sys.argv))
