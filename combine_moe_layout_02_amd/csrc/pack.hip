@@ -132,52 +132,72 @@ __global__ __launch_bounds__(kPartThreads) void pack_dedup_kernel(
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> OCP E4M3FN code, round to nearest even, saturating to +-448. q must not be NaN.
-__device__ inline uint32_t e4m3fn_code(float q) {
-    const uint32_t u = __float_as_uint(q);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {  // |q| >= 448: largest finite code
-        code = 0x7Eu;
-    } else if (a < 0x3C800000u) {  // |q| < 2^-6: subnormal spacing 2^-9
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scale, RNE
-    } else {
-        // keep 3 mantissa bits: add just under half an ulp plus the kept lsb, then truncate;
-        // a carry into the exponent is the correct round-up to the next binade
-        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-        code = r - (120u << 3);  // rebias exponent 127 -> 7 in the 4.3 layout
-    }
-    return code | sign;
-}
-
 // fp32 -> INT8 code (two's complement byte): round half to even, clamp to [-127, 127].
 __device__ inline uint32_t int8_code(float q) {
-    const float r = fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(q), -127.0f, 127.0f);
     return (uint32_t)((int32_t)r) & 0xFFu;
-}
-
-template <int QUANT>
-__device__ inline uint32_t code_of(float q) {
-    if constexpr (QUANT == MOE_QUANT_FP8_E4M3_DYN) return e4m3fn_code(q);
-    else return int8_code(q);
 }
 
 // Largest code magnitude: the row's amax maps onto it.
 template <int QUANT>
 constexpr float code_max() { return QUANT == MOE_QUANT_FP8_E4M3_DYN ? 448.0f : 127.0f; }
 
-// Four bf16 pairs (two input words) -> four codes in one word, element order kept.
-template <int QUANT>
-__device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
-    return code_of<QUANT>(bf16_lo(w0) / scale) | (code_of<QUANT>(bf16_hi(w0) / scale) << 8) |
-           (code_of<QUANT>(bf16_lo(w1) / scale) << 16) | (code_of<QUANT>(bf16_hi(w1) / scale) << 24);
+// Smallest scale the reciprocal division below handles; rows with a smaller (or a non-finite)
+// scale divide with the IEEE division itself.
+constexpr float kFastDivMinScale = 0x1p-90f;
+
+// RN(x / scale) for scale in [2^-90, FLT_MAX], with y = RN(1 / scale): two FMA corrections of
+// q = x * y (Markstein's correction step; the first brings q within one ulp of x / scale, the
+// second rounds it correctly because y is the correctly rounded reciprocal). The exact remainder
+// needs |x| above 2^-103, which every quotient that can change a code has (|x / scale| >= 2^-11
+// with scale >= 2^-90); copysign keeps the sign of a zero x, which the corrections would turn
+// into +0. Compared on MI355X with the IEEE division for every finite bf16 x and 90,600 scales
+// (random, power-of-two neighbours, and every amax / 448 and amax / 127 of a bf16 amax): the
+// quotients agree for every |x / scale| in [2^-11, 449], and the codes for every x.
+__device__ inline float div_by_scale(float x, float scale, float y) {
+    const float q0 = x * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, scale, x), y, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, scale, x), y, q1);
+    return __builtin_copysignf(q2, x);
+}
+
+template <bool FAST>
+__device__ inline float quotient(float x, float scale, float y) {
+    if constexpr (FAST) return div_by_scale(x, scale, y);
+    else return x / scale;  // IEEE round-to-nearest division
+}
+
+// Four bf16 pairs (two input words) -> four codes in one word, element order kept. E4M3FN codes
+// come from gfx950's packed fp8 convert (round to nearest even) after a clamp to +-448, which
+// gives the saturating form; the pair compared equal to a bit-level RNE encoder on MI355X for
+// every finite fp32 input of either sign.
+template <int QUANT, bool FAST>
+__device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale, float y) {
+    const float q0 = quotient<FAST>(bf16_lo(w0), scale, y), q1 = quotient<FAST>(bf16_hi(w0), scale, y);
+    const float q2 = quotient<FAST>(bf16_lo(w1), scale, y), q3 = quotient<FAST>(bf16_hi(w1), scale, y);
+    if constexpr (QUANT == MOE_QUANT_FP8_E4M3_DYN) {
+        const float lim = code_max<QUANT>();
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q0, -lim, lim),
+                                                     __builtin_amdgcn_fmed3f(q1, -lim, lim), 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q2, -lim, lim),
+                                                 __builtin_amdgcn_fmed3f(q3, -lim, lim), packed, true);
+        return (uint32_t)packed;
+    } else {
+        return int8_code(q0) | (int8_code(q1) << 8) | (int8_code(q2) << 16) | (int8_code(q3) << 24);
+    }
+}
+
+template <int QUANT, bool FAST>
+__device__ inline u32x4 quant16(const u32x4 &a, const u32x4 &b, float scale, float y) {
+    return u32x4{quant4<QUANT, FAST>(a[0], a[1], scale, y), quant4<QUANT, FAST>(a[2], a[3], scale, y),
+                 quant4<QUANT, FAST>(b[0], b[1], scale, y), quant4<QUANT, FAST>(b[2], b[3], scale, y)};
 }
 
 // Quantises row t of x in one workgroup (blockDim.x >= ngroups, whole waves): lane u gets the 16
 // codes of elements [16u, 16u + 16) (zero past the row) and every lane the row's fp32 scale. The
 // row max is a wave shuffle reduction followed by an LDS reduction across waves (wave_max holds
-// one value per wave); scale = amax / top by IEEE division, codes from per-element IEEE divisions.
+// one value per wave); scale = amax / top by IEEE division, and every code from the correctly
+// rounded quotient x / scale (div_by_scale, or the IEEE division for extreme scales).
 template <int QUANT>
 __device__ inline void quantise_row(const uint8_t *__restrict__ x, int t, int ngroups,
                                     float *wave_max, u32x4 &codes, uint32_t &scale_bits) {
@@ -201,9 +221,12 @@ __device__ inline void quantise_row(const uint8_t *__restrict__ x, int t, int ng
 
     const float scale = amax / code_max<QUANT>();  // IEEE round-to-nearest division
     codes = u32x4{0u, 0u, 0u, 0u};
-    if (u < ngroups && amax > 0.0f)
-        codes = u32x4{quant4<QUANT>(a[0], a[1], scale), quant4<QUANT>(a[2], a[3], scale),
-                      quant4<QUANT>(b[0], b[1], scale), quant4<QUANT>(b[2], b[3], scale)};
+    if (u < ngroups && amax > 0.0f) {
+        if (scale >= kFastDivMinScale && scale <= 0x1.fffffep127f)  // the same for the whole row
+            codes = quant16<QUANT, true>(a, b, scale, 1.0f / scale);
+        else
+            codes = quant16<QUANT, false>(a, b, scale, 0.0f);
+    }
     scale_bits = __float_as_uint(scale);
 }
 

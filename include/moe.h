@@ -121,7 +121,9 @@ int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t
  *                           saturating to +-448;
  *   MOE_QUANT_INT8_DYN:     scale = amax / 127, codes = clamp(rint(x / scale), -127, 127), rint
  *                           rounding half to even, two's complement bytes;
- * every division an IEEE fp32 division; an all-zero row gives scale 0 and zero codes. Then the
+ * every division an IEEE fp32 division (codes are those of the correctly rounded quotient; x must
+ * be finite in these modes: a NaN or infinity gives unspecified codes); an all-zero row gives
+ * scale 0 and zero codes. Then the
  * scale block and the triple (src_rank, t, k). This is the CAM InputToShare copy with its
  * DynamicQuant branch ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6, whose quantised output
  * type is INT8, and the slot format of section 2.3), with each row read once per token instead of

@@ -260,6 +260,50 @@ def test_dispatch_tiny(moe, case):
                         oracle.slot_geometry(H, quant), str(case))
 
 
+def every_bf16_rows(amax_bits, H):
+    """Rows that pass every finite bf16 value of magnitude <= amax through the quantiser with the
+    row maximum amax: per amax, element 0 of each row is +-amax and the rest of the rows hold all
+    such values (both signs, -0.0 included), zero-filled at the end."""
+    finite = np.arange(1 << 16, dtype=np.uint32)
+    finite = finite[(finite & 0x7F80) != 0x7F80].astype(np.uint16)
+    mag = (finite.astype(np.uint32) << 16).view(np.float32)
+    rows = []
+    for i, ab in enumerate(amax_bits):
+        amax = float((np.uint32(ab) << 16).view(np.float32))
+        vals = finite[np.abs(mag) <= amax]
+        per = H - 1
+        for r0 in range(0, vals.size, per):
+            row = np.zeros(H, np.uint16)
+            row[0] = ab | (0x8000 if (r0 // per + i) % 2 else 0)
+            chunk = vals[r0 : r0 + per]
+            row[1 : 1 + chunk.size] = chunk
+            rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("quant", [1, 2])
+def test_dispatch_quant_every_bf16_value(moe, quant):
+    """Every finite bf16 value under row maxima that put the scale on a power of two (amax 448 or
+    127: the quotient is x itself), at the largest bf16, near the smallest scale of the reciprocal
+    division (448 * 2^-90 and one bf16 step either side) and far below it (subnormal amax), and at
+    random bf16 values. Codes and scales must equal the oracle's bit for bit."""
+    top = 448.0 if quant == 1 else 127.0
+    special = [top, top * 2.0 ** -90, top * 2.0 ** 60, 3.3895313892515355e38, 2.0 ** -133, 1e-30]
+    bits = list(f32_to_bf16_input(np.array(special, np.float32)).astype(np.uint32))
+    edge = int(f32_to_bf16_input(np.array([top * 2.0 ** -90], np.float32))[0])
+    bits += [edge - 1, edge + 1]
+    rng = np.random.default_rng(40 + quant)
+    bits += list(rng.integers(0x0080, 0x7F7F, 10))
+    H = 8192
+    xb = every_bf16_rows([int(b) & 0x7FFF for b in bits], H)
+    S = xb.shape[0]
+    slot = np.arange(S, dtype=np.int32).reshape(S, 1)
+    note(f"dispatch every bf16 value quant {quant}: S={S} H={H}")
+    win = gpu_dispatch(moe, xb, slot, quant)
+    assert_window_equal(win, oracle.dispatch_slots(xb, slot, quant, 0),
+                        oracle.slot_geometry(H, quant), f"every bf16 quant {quant}")
+
+
 def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
