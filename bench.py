@@ -13,7 +13,9 @@ the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); ext
 one set of buffers. extras.copy_ceiling_GB/s is a 1 GiB device-to-device copy.
 extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
-bounds the event timings at decode sizes.
+bounds the event timings at decode sizes. extras.graph_replay_fused_layout_dispatch
+does the same with the layout and the pack in one moe_layout_dispatch call (one
+kernel for decode-sized tables).
 
 kernels: event statistics per call (layout, dispatch = the pack, combine) and
 for the sums layout+dispatch and layout+dispatch+combine, each with its bytes,
@@ -135,22 +137,27 @@ def copy_ceiling(torch, dev, mib=1024, iters=10):
     return gbs
 
 
-def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
+def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False):
     """The same step captured once per input set in a HIP graph and replayed: the device time of a
-    step without the Python launch overhead, which dominates at decode sizes."""
+    step without the Python launch overhead, which dominates at decode sizes. fused: the layout and
+    the pack through moe_layout_dispatch (one kernel when S*K <= 4096 and C <= 1024)."""
+    def step(x, topk, wts, eo):
+        if fused:
+            moe.moe_layout_dispatch(topk, w.E, w.P, C, x, window, w.quant, 0, out=lay)
+        else:
+            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
     graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     for x, topk, wts, eo in sets:
         with torch.cuda.stream(side):  # warm-up on the capture stream
-            moe.moe_layout(topk, w.E, w.P, C, out=lay)
-            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
-            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+            step(x, topk, wts, eo)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            moe.moe_layout(topk, w.E, w.P, C, out=lay)
-            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
-            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+            step(x, topk, wts, eo)
         graphs.append(g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
@@ -448,6 +455,9 @@ def main():
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                           total_bytes)
+        fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
+        fused["one_kernel_layout_dispatch"] = w.S * w.K <= 4096 and C <= 1024
+        out["extras"]["graph_replay_fused_layout_dispatch"] = fused
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],

@@ -30,7 +30,7 @@ MOE_QUANT_INT8_DYN = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
-    "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "moe_unpack_padded",
+    "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "moe_unpack_padded",
     "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 )
@@ -54,6 +54,8 @@ def _load():
         "moe_slot_offsets": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
+        "moe_layout_dispatch": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
+                                [P, I32, I32, I32, P, I64, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
         "moe_combine_scatter": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, I64, I64, P]),
         "moe_combine_staged": (ctypes.c_int, [P, I64, P, P, I32, I32, I32, P, P]),
@@ -193,6 +195,32 @@ def moe_dispatch(x, slot_idx, window, quant=MOE_QUANT_NONE, src_rank=0, stream=N
     _check(_lib.moe_dispatch(_ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank),
                              _ptr(window), nbytes, _stream(x.device, stream)))
     return window
+
+
+def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, window,
+                        quant=MOE_QUANT_NONE, src_rank=0, out=None, stream=None):
+    """moe_layout and moe_dispatch in one call (one kernel for small tables); returns the Layout."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    dev = topk_idx.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(window, "window", device=dev)
+    S, K = topk_idx.shape
+    if x.shape[0] != S:
+        raise ValueError("x must have one row per token of topk_idx")
+    H = x.shape[1]
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    if out is None:
+        out = empty_layout(S, K, E, P, C, dev)
+    shapes = [(S, P), (P,), (E,), (P, C), (E, C), (P + 1,), (E + 1,), (S, K), (1,)]
+    for name, t, shp in zip(Layout._fields, out, shapes):
+        _need(t, name, torch.bool if name == "is_token_in_rank" else torch.int32, device=dev)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                                    _ptr(x), H, int(quant), int(src_rank), _ptr(window), nbytes,
+                                    _stream(dev, stream)))
+    return out
 
 
 def moe_combine(expert_out, slot_idx, topk_weights, row_stride_bytes=None, expert_rows=None,
@@ -468,7 +496,7 @@ __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_dispatch", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 ]

@@ -405,13 +405,12 @@ hipError_t launch_count(const int32_t *topk_idx, int S, int K, int E, int P, int
     return hipGetLastError();
 }
 
-// MOE_LAYOUT_SMALL=0 in the environment turns the single-launch path off (read on every call).
+}  // namespace
+
 bool layout_small_enabled() {
     const char *v = getenv("MOE_LAYOUT_SMALL");
     return !(v && v[0] == '0');
 }
-
-}  // namespace
 
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                          int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,

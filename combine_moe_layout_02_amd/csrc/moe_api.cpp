@@ -112,6 +112,44 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
 }
 
+int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                        int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                        int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                        int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                        int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                        const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                        int64_t window_bytes, hipStream_t stream) {
+    if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
+        !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
+        !slot_idx || !status || !x || !window)
+        return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    if (E % P != 0) return MOE_ERR_UNSUPPORTED;
+    const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
+                         expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
+    for (const void *p : i32)
+        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(window, 512)) return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    if (moe::layout_small_enabled() && moe::layout_small_fits(S, K, E, P, C))
+        return from_hip(moe::launch_layout_dispatch_small(
+            topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
+            rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
+            status, x, H, quant, src_rank, window, stream));
+    st = from_hip(moe::launch_layout(topk_idx, S, K, E, P, C, is_token_in_rank,
+                                     num_tokens_per_rank, num_tokens_per_expert,
+                                     rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
+                                     expert_slot_base, slot_idx, status, stream));
+    if (st != MOE_OK) return st;
+    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+}
+
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                 const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
                 int32_t K, void *y, hipStream_t stream) {

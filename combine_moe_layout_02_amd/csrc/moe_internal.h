@@ -42,6 +42,10 @@ constexpr int kSmallLayoutChannels = 1024;  // C
 // True when the single-launch layout can take (S, K, E, P, C).
 bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C);
 
+// False when MOE_LAYOUT_SMALL=0 is set in the environment (read on every call): then the
+// three-launch layout runs even for small tables.
+bool layout_small_enabled();
+
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                          int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
@@ -56,6 +60,15 @@ hipError_t launch_layout_small(const int32_t *topk_idx, int32_t S, int32_t K, in
                                int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                                int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                                hipStream_t stream);
+
+// Layout and pack of a small table (layout_small_fits) in one launch; same outputs as
+// launch_layout_small followed by launch_pack.
+hipError_t launch_layout_dispatch_small(
+    const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+    uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+    int32_t *rank_prefix_matrix, int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+    int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, const void *x, int32_t H,
+    int32_t quant, int32_t src_rank, void *window, hipStream_t stream);
 
 hipError_t launch_rank_rows(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                             int32_t C, const int32_t *rank_prefix_matrix,

@@ -140,6 +140,27 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
                  int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                  hipStream_t stream);
 
+/* Layout and dispatch pack in one call: the outputs of moe_layout (same arguments, same meaning)
+ * and the window of moe_dispatch (same x, H, quant, src_rank, window, window_bytes), bit for bit.
+ * It is the fused single-kernel layout + pack for decode-sized batches, where both steps are
+ * latency: the routing plan of "Ascend DeepEP MoE Dispatch Optimization" (section "Dispatch handle
+ * 六项分别保存什么") and the InputToShare copy of "HCCL Window 模式 (Non-SHMEM) 代码深度剖析"
+ * (section 3.6) without a launch between them.
+ *
+ * When S*K <= 4096 and C <= 1024 (and MOE_LAYOUT_SMALL is not 0) it enqueues ONE kernel: its
+ * layout workgroups write the layout outputs while its pack workgroups derive the slots of their
+ * own tokens from topk_idx (the number of valid entries before (t, k) in expert-major, token, k
+ * order) and store the rows; nothing in it reads slot_idx. Otherwise it enqueues the moe_layout
+ * kernels followed by the moe_dispatch kernel. Argument checks, alignment rules and error codes
+ * are the union of the two calls'; the window must not overlap any other argument. */
+int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                        int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                        int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                        int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                        int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                        const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                        int64_t window_bytes, hipStream_t stream);
+
 /* Combine: y[t] = bf16( sum over k = 0..K-1 ascending with slot_idx[t, k] valid of
  *                       fp32(topk_weights[t, k] * fp32(expert_out row slot_idx[t, k])) ),
  * accumulated in fp32 from +0.0, each product and each sum rounded to fp32 (no fused

@@ -32,6 +32,9 @@ int main(void) {
           "moe_layout rejects E % P != 0");
     check(moe_dispatch(dev, dev, 64, 7168, 8, MOE_QUANT_NONE, 0, dev, 100, NULL) == MOE_ERR_WINDOW,
           "moe_dispatch rejects a small window");
+    check(moe_layout_dispatch(dev, 64, 8, 256, 8, 16, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev,
+                              7168, MOE_QUANT_FP8_E4M3_DYN, 0, dev, 100, NULL) == MOE_ERR_WINDOW,
+          "moe_layout_dispatch rejects a small window");
     check(moe_combine(dev, 14336, 512, dev, dev, 64, 7168, 8, (char *)dev + 8, NULL) == MOE_ERR_ALIGN,
           "moe_combine rejects a misaligned y");
     check(strlen(moe_status_string(MOE_ERR_WINDOW)) > 0, "moe_status_string");

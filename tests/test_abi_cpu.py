@@ -101,6 +101,39 @@ def test_dispatch_validation(kw, err):
     assert dispatch_call(**kw) == err
 
 
+def layout_dispatch_call(topk=A, S=64, K=8, E=256, P=8, C=16, outs=None, x=A, H=7168, quant=0,
+                         window=A, nbytes=None):
+    outs = outs if outs is not None else [A] * 9
+    if nbytes is None:
+        nbytes = S * K * 14848
+    return moe._lib.moe_layout_dispatch(topk, S, K, E, P, C, *outs, x, H, quant, 0, window, nbytes,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(topk=NULL), moe.MOE_ERR_ARG),
+    (dict(outs=[A] * 8 + [NULL]), moe.MOE_ERR_ARG),
+    (dict(x=NULL), moe.MOE_ERR_ARG),
+    (dict(window=NULL), moe.MOE_ERR_ARG),
+    (dict(S=0), moe.MOE_ERR_ARG),
+    (dict(K=17), moe.MOE_ERR_ARG),
+    (dict(E=250, P=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(C=65), moe.MOE_ERR_ARG),
+    (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
+    (dict(H=8), moe.MOE_ERR_ARG),
+    (dict(quant=3), moe.MOE_ERR_ARG),
+    (dict(topk=A + 2), moe.MOE_ERR_ALIGN),
+    (dict(outs=[A] * 7 + [A + 1, A]), moe.MOE_ERR_ALIGN),
+    (dict(x=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(window=A + 256), moe.MOE_ERR_ALIGN),
+    (dict(nbytes=64 * 8 * 14848 - 1), moe.MOE_ERR_WINDOW),
+    (dict(S=8192, K=8, C=128, nbytes=8192 * 8 * 14848 - 512), moe.MOE_ERR_WINDOW),
+])
+def test_layout_dispatch_validation(kw, err):
+    """The union of moe_layout's and moe_dispatch's checks, all before any HIP call."""
+    assert layout_dispatch_call(**kw) == err
+
+
 def combine_call(eo=A, stride=14336, rows=512, slot=A, w=A, S=64, H=7168, K=8, y=A):
     return moe._lib.moe_combine(eo, stride, rows, slot, w, S, H, K, y, None)
 

@@ -188,6 +188,70 @@ def test_layout_special_tables(moe, layout_path):
             assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), name)
 
 
+# ---------------------------------------------------------------- layout + dispatch in one call
+
+
+def gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank=0):
+    S, K = idx.shape
+    H = x_bits.shape[1]
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    lay = moe.moe_layout_dispatch(to_dev(idx), E, P, C, bf16_dev(x_bits), win, quant, src_rank,
+                                  out=poisoned_layout(moe, S, K, E, P, C))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in lay._asdict().items()}, win.cpu().numpy().reshape(S * K, -1)
+
+
+def check_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank, what):
+    got, win = gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank)
+    ref = oracle.layout(idx, E, P, C)
+    assert_layout_equal(got, ref, what)
+    H = x_bits.shape[1]
+    assert_window_equal(win, oracle.dispatch_slots(x_bits, ref["slot_idx"], quant, src_rank),
+                        oracle.slot_geometry(H, quant), what)
+
+
+@pytest.mark.parametrize("cfg,quant", [(1, 0), (1, 1), (2, 0), (2, 1), (2, 2), (3, 0)])
+def test_layout_dispatch_workloads(moe, cfg, quant, layout_path):
+    """One call for the layout and the pack: one kernel at workloads 1 and 2, the separate kernels
+    at workload 3 (and everywhere with MOE_LAYOUT_SMALL=0)."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    note(f"layout_dispatch cfg{cfg} quant {quant} path={layout_path}")
+    check_layout_dispatch(moe, inp["topk_idx"], inp["x"], w.E, w.P, w.C, quant, 5,
+                          f"cfg{cfg} quant {quant}")
+
+
+FUSED_CASES = [
+    # (S, K, H, E, P, C, quant, p_mask, p_bad, seed)
+    (1, 1, 16, 1, 1, 1, 0, 0.0, 0.0, 31),
+    (5, 3, 48, 6, 3, 2, 1, 0.3, 0.0, 32),
+    (37, 4, 2064, 12, 4, 3, 2, 0.2, 0.1, 33),      # bad ids: status bit 0, no slot
+    (300, 13, 1024, 512, 1, 7, 0, 0.1, 0.0, 34),   # E at its maximum, one rank
+    (512, 8, 7168, 256, 8, 128, 0, 0.0, 0.0, 35),  # S*K = 4096: the largest one-kernel table
+    (512, 8, 7168, 256, 8, 128, 1, 0.05, 0.0, 36),
+    (513, 8, 1024, 256, 8, 128, 2, 0.0, 0.0, 37),  # one token more: separate kernels
+    (4096, 1, 256, 16, 4, 1000, 1, 0.1, 0.0, 38),  # 4096 tokens over 256 pack workgroups
+    (4096, 1, 256, 16, 4, 1000, 0, 0.1, 0.0, 39),
+    (64, 8, 7168, 512, 256, 64, 1, 0.1, 0.05, 40),
+    (128, 16, 16384, 64, 8, 128, 0, 0.0, 0.0, 41),  # largest H and K: row split in 2 parts
+    (128, 16, 16384, 64, 8, 128, 2, 0.2, 0.0, 42),
+    (200, 3, 4112, 9, 3, 7, 0, 0.0, 0.0, 43),       # ragged channels, H not a multiple of 512 B
+    (96, 4, 64, 16, 4, 3, 0, 1.0, 0.0, 44),         # everything masked: nothing written
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+def test_layout_dispatch_tiny(moe, case, layout_path):
+    S, K, H, E, P, C, quant, p_mask, p_bad, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
+    x = rng.standard_normal((S, H)).astype(np.float32) * 3
+    x[0, :] = 0.0
+    xb = f32_to_bf16_input(x)
+    note(f"layout_dispatch tiny {case} path={layout_path}")
+    check_layout_dispatch(moe, idx, xb, E, P, C, quant, seed, str(case))
+
+
 # ---------------------------------------------------------------- dispatch
 
 
