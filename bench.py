@@ -69,10 +69,12 @@ def traffic_from_profiles(kernel_key):
             return None
         import hashlib
 
-        src = os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", rec["source"])
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None  # the kernel changed since the counters were taken
+        h = hashlib.sha256()
+        for name in rec["sources"]:  # the kernel's file and the headers it includes
+            with open(os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None  # the kernel changed since the counters were taken
         return rec["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None

@@ -1,10 +1,11 @@
 // Native consumer of include/moe.h on the GPU: no Python, no torch. Reads a routing table, x,
-// weights and expert rows from the binary input file, runs moe_layout -> moe_dispatch ->
-// moe_combine on hipMalloc'd buffers through libmoe.so, and writes slot_idx, the dispatched slot
-// regions and y to the output file for the test to compare with the oracle.
+// weights and expert rows from the binary input file, runs moe_layout -> moe_dispatch (or both
+// through moe_layout_dispatch when `fused` is 1) -> moe_combine on hipMalloc'd buffers through
+// libmoe.so, and writes slot_idx, the dispatched slot regions and y to the output file for the
+// test to compare with the oracle.
 //
-// Input file: int32 S, K, H, E, P, C, quant; int32 topk[S*K]; uint16 x[S*H]; float w[S*K];
-//             uint16 expert_out[S*K*H].
+// Input file: int32 S, K, H, E, P, C, quant, fused; int32 topk[S*K]; uint16 x[S*H];
+//             float w[S*K]; uint16 expert_out[S*K*H].
 // Output file: int32 status; int32 slot_idx[S*K]; uint8 window[S*K*slot_bytes]; uint16 y[S*H].
 #include <hip/hip_runtime.h>
 
@@ -44,9 +45,10 @@ int main(int argc, char **argv) {
     }
     FILE *in = std::fopen(argv[1], "rb");
     if (!in) return 1;
-    int32_t hdr[7];
-    if (std::fread(hdr, sizeof(int32_t), 7, in) != 7) return 1;
+    int32_t hdr[8];
+    if (std::fread(hdr, sizeof(int32_t), 8, in) != 8) return 1;
     const int32_t S = hdr[0], K = hdr[1], H = hdr[2], E = hdr[3], P = hdr[4], C = hdr[5], quant = hdr[6];
+    const bool fused = hdr[7] != 0;
     std::vector<int32_t> topk;
     std::vector<uint16_t> x, eo;
     std::vector<float> w;
@@ -86,9 +88,14 @@ int main(int argc, char **argv) {
     CHECK_HIP(hipMemcpy(d_w, w.data(), sizeof(float) * S * K, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemset(d_window, 0xAB, window_bytes));
 
-    CHECK_MOE(moe_layout(d_topk, S, K, E, P, C, d_in_rank, d_npr, d_npe, d_rpm, d_epm, d_rsb, d_esb, d_slot,
-                         d_status, stream));
-    CHECK_MOE(moe_dispatch(d_x, d_slot, S, H, K, quant, 0, d_window, window_bytes, stream));
+    if (fused) {
+        CHECK_MOE(moe_layout_dispatch(d_topk, S, K, E, P, C, d_in_rank, d_npr, d_npe, d_rpm, d_epm, d_rsb, d_esb,
+                                      d_slot, d_status, d_x, H, quant, 0, d_window, window_bytes, stream));
+    } else {
+        CHECK_MOE(moe_layout(d_topk, S, K, E, P, C, d_in_rank, d_npr, d_npe, d_rpm, d_epm, d_rsb, d_esb, d_slot,
+                             d_status, stream));
+        CHECK_MOE(moe_dispatch(d_x, d_slot, S, H, K, quant, 0, d_window, window_bytes, stream));
+    }
     CHECK_MOE(moe_combine(d_eo, 2 * (int64_t)H, (int64_t)S * K, d_slot, d_w, S, H, K, d_y, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
 
@@ -113,6 +120,6 @@ int main(int argc, char **argv) {
                     d_x, d_eo, d_y, d_w};
     for (void *b : bufs) CHECK_HIP(hipFree(b));
     CHECK_HIP(hipStreamDestroy(stream));
-    std::printf("abi_gpu ok: S=%d K=%d H=%d E=%d P=%d C=%d quant=%d\n", S, K, H, E, P, C, quant);
+    std::printf("abi_gpu ok: S=%d K=%d H=%d E=%d P=%d C=%d quant=%d fused=%d\n", S, K, H, E, P, C, quant, (int)fused);
     return 0;
 }

@@ -1,5 +1,6 @@
 """The C ABI from a native C++ program on the GPU (tests/c_abi/abi_gpu.cpp): hipMalloc'd buffers,
-moe_layout -> moe_dispatch -> moe_combine through libmoe.so, no Python or torch in the process.
+moe_layout -> moe_dispatch (or moe_layout_dispatch) -> moe_combine through libmoe.so, no Python or
+torch in the process.
 Its outputs are compared with the oracle bit for bit. The program is built with the library
 (combine_moe_layout_02_amd/build.py)."""
 
@@ -18,16 +19,16 @@ pytestmark = pytest.mark.gpu
 EXE = os.path.join(ROOT, "tests", "c_abi", "abi_gpu")
 
 
-def _run_native(tmp_path, S, K, H, E, P, C, quant, inp):
+def _run_native(tmp_path, S, K, H, E, P, C, quant, inp, fused=0):
     assert os.path.exists(EXE), f"{EXE} is missing: run python combine_moe_layout_02_amd/build.py"
     src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(src, "wb") as f:
-        f.write(np.array([S, K, H, E, P, C, quant], np.int32).tobytes())
+        f.write(np.array([S, K, H, E, P, C, quant, fused], np.int32).tobytes())
         f.write(np.ascontiguousarray(inp["topk_idx"], np.int32).tobytes())
         f.write(np.ascontiguousarray(inp["x"], np.uint16).tobytes())
         f.write(np.ascontiguousarray(inp["topk_weights"], np.float32).tobytes())
         f.write(np.ascontiguousarray(inp["expert_out"], np.uint16).tobytes())
-    print(f"native abi program: S={S} K={K} H={H} E={E} P={P} C={C} quant={quant}", flush=True)
+    print(f"native abi program: S={S} K={K} H={H} E={E} P={P} C={C} quant={quant} fused={fused}", flush=True)
     res = subprocess.run([EXE, str(src), str(dst)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     raw = dst.read_bytes()
@@ -51,10 +52,10 @@ def _run_native(tmp_path, S, K, H, E, P, C, quant, inp):
     assert np.array_equal(y, oracle.combine(inp["expert_out"], ref["slot_idx"], inp["topk_weights"]))
 
 
-@pytest.mark.parametrize("cfg,quant", [(1, 0), (1, 1), (2, 2)])
-def test_native_program_matches_oracle(tmp_path, cfg, quant):
+@pytest.mark.parametrize("cfg,quant,fused", [(1, 0, 0), (1, 1, 0), (2, 2, 0), (1, 0, 1), (2, 1, 1)])
+def test_native_program_matches_oracle(tmp_path, cfg, quant, fused):
     w = WORKLOADS[cfg]
-    _run_native(tmp_path, w.S, w.K, w.H, w.E, w.P, w.C, quant, make_inputs(w))
+    _run_native(tmp_path, w.S, w.K, w.H, w.E, w.P, w.C, quant, make_inputs(w), fused)
 
 
 def test_native_program_masked_and_bad_ids(tmp_path):
@@ -69,3 +70,4 @@ def test_native_program_masked_and_bad_ids(tmp_path):
         "expert_out": draw_expert_out(7101, S * K, H),
     }
     _run_native(tmp_path, S, K, H, E, P, C, 0, inp)
+    _run_native(tmp_path, S, K, H, E, P, C, 1, inp, fused=1)
