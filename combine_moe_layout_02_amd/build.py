@@ -68,16 +68,22 @@ def build(verbose=False, extra_flags=()):
 
 
 def build_abi_harness(verbose=False):
-    """The C++ consumer of the C ABI used by the GPU tests (tests/c_abi/abi_gpu.cpp), linked
-    against libmoe.so; lands next to its source."""
-    src = os.path.join(ROOT, "tests", "c_abi", "abi_gpu.cpp")
-    exe = os.path.join(ROOT, "tests", "c_abi", "abi_gpu")
-    cmd = [hipcc(), "-x", "hip", "-O2", "-std=c++17", f"--offload-arch={ARCH}", f"-I{INCLUDE}", src, "-o",
-           exe, f"-L{PKG}", "-lmoe", f"-Wl,-rpath,{PKG}"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    _run(cmd)
-    return exe
+    """The native test programs the GPU tests run, each landing next to its source:
+    tests/c_abi/abi_gpu.cpp, a C++ consumer of the C ABI linked against libmoe.so, and
+    tests/c_abi/quant_gpu.cpp, which runs the pack's quantisation helpers (csrc/pack_rows.h) over
+    every fp32 code boundary and every bf16 quotient, compiled with the library's flags."""
+    c_abi = os.path.join(ROOT, "tests", "c_abi")
+    abi = os.path.join(c_abi, "abi_gpu")
+    cmds = [[hipcc(), "-x", "hip", "-O2", "-std=c++17", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
+             os.path.join(c_abi, "abi_gpu.cpp"), "-o", abi, f"-L{PKG}", "-lmoe", f"-Wl,-rpath,{PKG}"]]
+    quant = os.path.join(c_abi, "quant_gpu")
+    flags = [f for f in FLAGS if f not in ("-fPIC",)]
+    cmds.append([hipcc(), "-x", "hip", *flags, os.path.join(c_abi, "quant_gpu.cpp"), "-o", quant])
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        _run(cmd)
+    return [abi, quant]
 
 
 if __name__ == "__main__":

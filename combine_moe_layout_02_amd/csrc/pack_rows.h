@@ -76,24 +76,28 @@ __device__ inline float quotient(float x, float scale, float y) {
     else return x / scale;  // IEEE round-to-nearest division
 }
 
-// Four bf16 pairs (two input words) -> four codes in one word, element order kept. E4M3FN codes
-// come from gfx950's packed fp8 convert (round to nearest even) after a clamp to +-448, which
-// gives the saturating form; the pair compared equal to a bit-level RNE encoder on MI355X for
-// every finite fp32 input of either sign.
+// Four fp32 values -> four E4M3FN codes in one word (element order kept): gfx950's packed fp8
+// convert (round to nearest even) after a clamp to +-448, which gives the saturating form. It
+// equals a bit-level RNE encoder for every finite fp32 input of either sign (tests/c_abi/quant_gpu.cpp
+// checks every non-negative finite input against the oracle's code boundaries).
+__device__ inline uint32_t e4m3fn_pack4(float q0, float q1, float q2, float q3) {
+    constexpr float lim = 448.0f;
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q0, -lim, lim),
+                                                 __builtin_amdgcn_fmed3f(q1, -lim, lim), 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q2, -lim, lim),
+                                             __builtin_amdgcn_fmed3f(q3, -lim, lim), packed, true);
+    return (uint32_t)packed;
+}
+
+// Four bf16 pairs (two input words) -> four codes in one word, element order kept.
 template <int QUANT, bool FAST>
 __device__ inline uint32_t quant4(uint32_t w0, uint32_t w1, float scale, float y) {
     const float q0 = quotient<FAST>(bf16_lo(w0), scale, y), q1 = quotient<FAST>(bf16_hi(w0), scale, y);
     const float q2 = quotient<FAST>(bf16_lo(w1), scale, y), q3 = quotient<FAST>(bf16_hi(w1), scale, y);
-    if constexpr (QUANT == MOE_QUANT_FP8_E4M3_DYN) {
-        const float lim = code_max<QUANT>();
-        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q0, -lim, lim),
-                                                     __builtin_amdgcn_fmed3f(q1, -lim, lim), 0, false);
-        packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q2, -lim, lim),
-                                                 __builtin_amdgcn_fmed3f(q3, -lim, lim), packed, true);
-        return (uint32_t)packed;
-    } else {
+    if constexpr (QUANT == MOE_QUANT_FP8_E4M3_DYN)
+        return e4m3fn_pack4(q0, q1, q2, q3);
+    else
         return int8_code(q0) | (int8_code(q1) << 8) | (int8_code(q2) << 16) | (int8_code(q3) << 24);
-    }
 }
 
 template <int QUANT, bool FAST>
