@@ -22,8 +22,6 @@
 // Nothing scans the [S, P] matrix: everything is derived from the K ids of each token.
 // Small tables (decode-sized batches) take the single-launch path in layout_small.hip instead.
 
-#include <stdlib.h>
-
 #include "moe_internal.h"
 
 namespace moe {
@@ -407,10 +405,6 @@ hipError_t launch_count(const int32_t *topk_idx, int S, int K, int E, int P, int
 
 }  // namespace
 
-bool layout_small_enabled() {
-    const char *v = getenv("MOE_LAYOUT_SMALL");
-    return !(v && v[0] == '0');
-}
 
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                          int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,

@@ -489,12 +489,6 @@ hipError_t launch_fused(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
 
 }  // namespace
 
-bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
-    (void)E;
-    (void)P;
-    return (int64_t)S * K <= kSmallLayoutEntries && C <= kSmallLayoutChannels;
-}
-
 hipError_t launch_layout_small(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                                int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                                int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,

@@ -7,6 +7,7 @@
 // DeepEP Python entry ("Ascend DeepEP MoE Dispatch Optimization", section "从 Python 接口进入真实调用链").
 
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "moe_internal.h"
 
@@ -28,6 +29,12 @@ int check_tokens(int32_t S, int32_t K) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// True when rows [0, rows) at `stride` bytes apart have byte offsets an int64 can hold (rows * stride
+// <= INT64_MAX), so the kernels' row addresses cannot wrap.
+bool extent_fits(int64_t rows, int64_t stride) {
+    return rows <= 1 || stride <= INT64_MAX / rows;
+}
+
 int check_experts(int32_t E, int32_t P) {
     if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
     if (E % P != 0) return MOE_ERR_UNSUPPORTED;
@@ -35,6 +42,21 @@ int check_experts(int32_t E, int32_t P) {
 }
 
 }  // namespace
+
+namespace moe {
+
+bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
+    (void)E;
+    (void)P;
+    return (int64_t)S * K <= kSmallLayoutEntries && C <= kSmallLayoutChannels;
+}
+
+bool layout_small_enabled() {
+    const char *v = getenv("MOE_LAYOUT_SMALL");
+    return !(v && v[0] == '0');
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -159,6 +181,7 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
     st = check_hidden(H);
     if (st != MOE_OK) return st;
     if (expert_rows < 0 || row_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
+    if (!extent_fits(expert_rows, row_stride_bytes)) return MOE_ERR_ARG;
     if (row_stride_bytes % 16 != 0 || !aligned(expert_out, 16) || !aligned(y, 16) ||
         !aligned(slot_idx, 4) || !aligned(topk_weights, 4))
         return MOE_ERR_ALIGN;
@@ -177,10 +200,13 @@ int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_
     if (st != MOE_OK) return st;
     if (expert_rows < 0 || expert_rows > MOE_MAX_OUT_ROWS) return MOE_ERR_ARG;
     if (row_stride_bytes < 2 * (int64_t)H || staging_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
+    if (!extent_fits(expert_rows, row_stride_bytes)) return MOE_ERR_ARG;
     if (row_stride_bytes % 16 != 0 || staging_stride_bytes % 16 != 0 || !aligned(expert_out, 16) ||
         !aligned(staging, 16) || !aligned(expand_idx, 4) || !aligned(num_rows, 4))
         return MOE_ERR_ALIGN;
-    if (staging_bytes < ((int64_t)S * K - 1) * staging_stride_bytes + 2 * (int64_t)H)
+    // staging_bytes >= (S*K - 1) * staging_stride_bytes + 2H, in a form that cannot overflow
+    if (staging_bytes < 2 * (int64_t)H ||
+        (staging_bytes - 2 * (int64_t)H) / staging_stride_bytes < (int64_t)S * K - 1)
         return MOE_ERR_WINDOW;
     return from_hip(moe::launch_combine_scatter(expert_out, row_stride_bytes, expert_rows,
                                                 expand_idx, num_rows, S, K, H, staging,

@@ -172,7 +172,8 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
  *                    row_stride_bytes >= 2H and a multiple of 16. Passing the window with
  *                    row_stride_bytes = moe_slot_bytes(H) combines the dispatched bf16 payload.
  *      expert_rows   number of readable rows; entries of slot_idx outside [0, expert_rows) are
- *                    skipped like pads.
+ *                    skipped like pads. expert_rows * row_stride_bytes must not exceed INT64_MAX
+ *                    (MOE_ERR_ARG otherwise).
  *      slot_idx      int32 [S, K]; topk_weights fp32 [S, K].
  * Out: y             bf16 [S, H], 16-byte aligned, fully overwritten; must not overlap the inputs. */
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
@@ -189,7 +190,8 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
  *
  * moe_combine_scatter
  * In:  expert_out     bf16 rows as for moe_combine (row s = the output for slot s); expert_rows
- *                     rows are readable, expert_rows in [0, MOE_MAX_OUT_ROWS].
+ *                     rows are readable, expert_rows in [0, MOE_MAX_OUT_ROWS], and
+ *                     expert_rows * row_stride_bytes must not exceed INT64_MAX.
  *      expand_idx     int32 [expert_rows, 3]: the (src_rank, t, k) triple of each row, e.g. from
  *                     moe_unpack.
  *      num_rows       DEVICE pointer to N (e.g. &expert_slot_base[E]); rows s >= min(N,

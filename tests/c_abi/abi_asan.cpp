@@ -1,0 +1,154 @@
+// Host-only run of the C ABI layer (combine_moe_layout_02_amd/csrc/moe_api.cpp) built with the
+// address and undefined-behaviour sanitizers against the stand-in launchers of abi_stubs.cpp:
+// the size arithmetic at the largest accepted sizes and at hostile int64 arguments, a rejected
+// call for every entry point, and which launchers a valid call reaches (for example that
+// moe_layout_dispatch takes the one-kernel path only for small tables). Pointers are fake device
+// addresses that nothing dereferences. Prints "abi_asan ok" and returns 0 when every check holds.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "abi_stubs.h"
+#include "moe.h"
+
+static int failures = 0;
+
+static void expect(bool cond, const char *what) {
+    if (!cond) {
+        std::printf("FAIL: %s\n", what);
+        ++failures;
+    }
+}
+
+static bool only(stubs::Launcher a, int na, stubs::Launcher b = stubs::kLaunchers, int nb = 0) {
+    for (int i = 0; i < stubs::kLaunchers; ++i) {
+        const int want = i == a ? na : (i == b ? nb : 0);
+        if (stubs::calls[i] != want) return false;
+    }
+    return true;
+}
+
+int main() {
+    char *base = reinterpret_cast<char *>(uintptr_t{1} << 20);  // 512-byte aligned, never touched
+    void *A = base;
+    int32_t *I = reinterpret_cast<int32_t *>(base);
+    uint8_t *U = reinterpret_cast<uint8_t *>(base);
+    float *F = reinterpret_cast<float *>(base);
+    const int64_t big = INT64_MAX;
+
+    // host functions at the limits
+    expect(moe_slot_bytes(7168) == 14848, "slot bytes at H=7168");
+    expect(moe_window_bytes(MOE_MAX_TOKENS, MOE_MAX_K, MOE_MAX_HIDDEN) ==
+               (int64_t)MOE_MAX_TOKENS * MOE_MAX_K * 33280,
+           "window bytes at the largest sizes");
+    expect(moe_window_bytes(MOE_MAX_TOKENS + 1, 1, 16) == MOE_ERR_UNSUPPORTED, "S above the limit");
+    expect(moe_dedup_window_bytes(MOE_MAX_TOKENS, MOE_MAX_K, MOE_MAX_RANKS, MOE_MAX_HIDDEN) ==
+               (int64_t)MOE_MAX_TOKENS * MOE_MAX_K * 33280,
+           "dedup window bytes at the largest sizes");
+    expect(moe_slot_offsets(MOE_MAX_HIDDEN, MOE_QUANT_FP8_E4M3_DYN, nullptr, nullptr, nullptr, nullptr) ==
+               MOE_OK,
+           "slot offsets with no outputs");
+    for (int st = -6; st <= 1; ++st) expect(moe_status_string(st) != nullptr, "status string");
+
+    // rejected calls: hostile sizes and int64 extremes
+    stubs::reset();
+    expect(moe_layout(I, 64, 8, 256, 8, 65, U, I, I, I, I, I, I, I, I, nullptr) == MOE_ERR_ARG, "layout C > S");
+    expect(moe_dispatch(A, I, 64, 7168, 8, 0, 0, A, -1, nullptr) == MOE_ERR_WINDOW, "dispatch negative window");
+    expect(moe_layout_dispatch(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 1, 0, A, 0, nullptr) ==
+               MOE_ERR_WINDOW,
+           "layout_dispatch empty window");
+    expect(moe_combine(A, big - 15, 1 << 20, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_ARG,
+           "combine row extent beyond int64");
+    expect(moe_combine(A, 14336, -1, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_ARG, "combine negative rows");
+    expect(moe_combine_scatter(A, 14336, 512, I, I, 64, 8, 7168, A, big - 15, big, nullptr) == MOE_ERR_WINDOW,
+           "scatter huge staging stride");
+    expect(moe_combine_scatter(A, big - 15, 512, I, I, 64, 8, 7168, A, 14336, big, nullptr) == MOE_ERR_ARG,
+           "scatter row extent beyond int64");
+    expect(moe_combine_scatter(A, 14336, 512, I, I, 64, 8, 7168, A, 14336, -5, nullptr) == MOE_ERR_WINDOW,
+           "scatter negative staging bytes");
+    expect(moe_combine_staged(A, 100, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_ARG, "staged short stride");
+    expect(moe_unpack(A, big, I, 64, 8, 7168, 1, A, nullptr, I, nullptr) == MOE_ERR_ARG, "unpack fp8 without scales");
+    expect(moe_unpack_padded(A, big, I, 256, 64, 8, 7168, 0, 16, big, A, nullptr, I, I, I, nullptr) == MOE_ERR_ARG,
+           "unpack_padded out_rows beyond the limit");
+    expect(moe_rank_rows(I, 64, 8, 250, 8, 16, I, I, I, I, nullptr) == MOE_ERR_UNSUPPORTED, "rank rows E % P");
+    expect(moe_dispatch_dedup(A, I, I, 64, 7168, 8, 256, 8, 0, 0, A, 1, nullptr) == MOE_ERR_WINDOW,
+           "dedup small window");
+    expect(moe_expand_dedup(A, big, I, I, I, 64, 8, 0, 7168, 0, A, nullptr, I, nullptr) == MOE_ERR_ARG,
+           "expand P = 0");
+    expect(only(stubs::kLaunchers, 0), "no launcher reached by a rejected call");
+
+    // valid calls and the launchers they reach
+    const int64_t win = moe_window_bytes(512, 8, 7168);
+    stubs::reset();
+    expect(moe_layout(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1),
+           "layout -> launch_layout");
+    stubs::reset();
+    expect(moe_layout_dispatch(I, 512, 8, 256, 8, 128, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win,
+                               nullptr) == MOE_OK &&
+               only(stubs::kLayoutDispatchSmall, 1),
+           "layout_dispatch at S*K = 4096 -> one kernel");
+    stubs::reset();
+    expect(moe_layout_dispatch(I, 513, 8, 256, 8, 128, U, I, I, I, I, I, I, I, I, A, 7168, 1, 0, A,
+                               moe_window_bytes(513, 8, 7168), nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1, stubs::kPack, 1),
+           "layout_dispatch at S*K = 4104 -> layout + pack");
+    stubs::reset();
+    expect(moe_layout_dispatch(I, 64, 8, 256, 8, 64, U, I, I, I, I, I, I, I, I, A, 7168, 2, 0, A, win, nullptr) ==
+                   MOE_OK &&
+               only(stubs::kLayoutDispatchSmall, 1),
+           "layout_dispatch small, int8");
+    stubs::reset();
+    expect(moe_layout_dispatch(I, 2048, 2, 16, 4, 1025, U, I, I, I, I, I, I, I, I, A, 16, 0, 0, A,
+                               moe_window_bytes(2048, 2, 16), nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1, stubs::kPack, 1),
+           "layout_dispatch with C above 1024 -> layout + pack");
+    setenv("MOE_LAYOUT_SMALL", "0", 1);
+    stubs::reset();
+    expect(moe_layout_dispatch(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win, nullptr) ==
+                   MOE_OK &&
+               only(stubs::kLayout, 1, stubs::kPack, 1),
+           "MOE_LAYOUT_SMALL=0 -> layout + pack");
+    unsetenv("MOE_LAYOUT_SMALL");
+    stubs::reset();
+    expect(moe_dispatch(A, I, 64, 7168, 8, 1, 3, A, win, nullptr) == MOE_OK && only(stubs::kPack, 1),
+           "dispatch -> launch_pack");
+    stubs::reset();
+    expect(moe_combine(A, 14848, 512, I, F, 64, 7168, 8, A, nullptr) == MOE_OK && only(stubs::kCombine, 1),
+           "combine -> launch_combine");
+    stubs::reset();
+    expect(moe_combine_scatter(A, 14336, 512, I, I, 64, 8, 7168, A, 14336, 512LL * 14336, nullptr) == MOE_OK &&
+               only(stubs::kCombineScatter, 1),
+           "combine_scatter with exactly S*K rows of staging");
+    expect(moe_combine_scatter(A, 14336, 512, I, I, 64, 8, 7168, A, 14336, 512LL * 14336 - 1, nullptr) ==
+               MOE_ERR_WINDOW,
+           "combine_scatter one byte short");
+    stubs::reset();
+    expect(moe_combine_staged(A, 14336, I, F, 64, 7168, 8, A, nullptr) == MOE_OK &&
+               only(stubs::kCombineStaged, 1),
+           "combine_staged");
+    stubs::reset();
+    expect(moe_unpack(A, win, I, 64, 8, 7168, 1, A, F, I, nullptr) == MOE_OK && only(stubs::kUnpack, 1),
+           "unpack");
+    stubs::reset();
+    expect(moe_unpack_padded(A, win, I, 256, 64, 8, 7168, 0, 16, MOE_MAX_OUT_ROWS, A, nullptr, I, I, I,
+                             nullptr) == MOE_OK &&
+               only(stubs::kUnpackPadded, 1),
+           "unpack_padded at the largest out_rows");
+    stubs::reset();
+    expect(moe_rank_rows(I, 64, 8, 256, 8, 16, I, I, I, I, nullptr) == MOE_OK && only(stubs::kRankRows, 1),
+           "rank_rows");
+    stubs::reset();
+    expect(moe_dispatch_dedup(A, I, I, 64, 7168, 8, 256, 8, 1, 0, A, moe_dedup_window_bytes(64, 8, 8, 7168),
+                              nullptr) == MOE_OK &&
+               only(stubs::kPackDedup, 1),
+           "dispatch_dedup");
+    stubs::reset();
+    expect(moe_expand_dedup(A, moe_dedup_window_bytes(64, 8, 8, 7168), I, I, I, 64, 8, 8, 7168, 2, A, F, I,
+                            nullptr) == MOE_OK &&
+               only(stubs::kExpandDedup, 1),
+           "expand_dedup");
+
+    if (failures == 0) std::printf("abi_asan ok\n");
+    return failures == 0 ? 0 : 1;
+}

@@ -727,26 +727,34 @@ def test_combine_from_window_round_trip(moe):
 # ---------------------------------------------------------------- determinism
 
 
-def test_repeat_runs_are_byte_identical(moe):
-    """Each kernel twice on identical inputs, outputs poisoned differently before each run."""
-    w = WORKLOADS[3]
-    inp = inputs(3)
+@pytest.mark.parametrize("cfg,quant,fused", [(3, 0, False), (2, 0, False), (2, 0, True), (2, 1, True),
+                                             (1, 2, True)])
+def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
+    """Each kernel twice on identical inputs, outputs poisoned differently before each run: the
+    three-launch layout (workload 3), the single-launch layout (workload 2) and the one-kernel
+    layout + pack (moe_layout_dispatch)."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
     idx = to_dev(inp["topk_idx"])
     x = bf16_dev(inp["x"])
-    eo = bf16_dev(expert_out(3))
+    eo = bf16_dev(expert_out(cfg))
     wts = to_dev(inp["topk_weights"])
     outs = []
+    note(f"determinism cfg{cfg} quant {quant} fused {fused}")
     for poison in (0x00, 0xFF):
         lay = moe.empty_layout(w.S, w.K, w.E, w.P, w.C, DEV)
         for t in lay:
             t.view(torch.uint8).fill_(poison)
-        moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
         win = torch.full((moe.moe_window_bytes(w.S, w.K, w.H),), poison, dtype=torch.uint8, device=DEV)
-        moe.moe_dispatch(x, lay.slot_idx, win, 0)
+        if fused:
+            moe.moe_layout_dispatch(idx, w.E, w.P, w.C, x, win, quant, out=lay)
+        else:
+            moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
+            moe.moe_dispatch(x, lay.slot_idx, win, quant)
         y = torch.full((w.S, w.H), float(poison), dtype=torch.bfloat16, device=DEV)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
         torch.cuda.synchronize()
-        g = oracle.slot_geometry(w.H, 0)
+        g = oracle.slot_geometry(w.H, quant)
         regions = win.view(w.S * w.K, -1)[:, : g.tail_end].cpu().numpy()
         outs.append(([t.cpu().numpy() for t in lay], regions, y.view(torch.int16).cpu().numpy()))
     (l0, r0, y0), (l1, r1, y1) = outs
@@ -787,10 +795,12 @@ def test_python_layer_rejects_bad_window(moe):
 # ---------------------------------------------------------------- graph capture
 
 
-def test_step_replays_from_a_captured_graph(moe):
-    """layout -> dispatch -> combine captured once in a HIP graph (the library allocates and
-    synchronises nothing) and replayed on fresh inputs copied into the captured buffers; every
-    replay must equal the eager result on the same inputs. Eager work runs between replays."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_replays_from_a_captured_graph(moe, fused):
+    """layout -> dispatch -> combine (or moe_layout_dispatch -> combine) captured once in a HIP
+    graph (the library allocates and synchronises nothing) and replayed on fresh inputs copied into
+    the captured buffers; every replay must equal the eager result on the same inputs. Eager work
+    runs between replays."""
     w = WORKLOADS[1]
     S, K, H, E, P, C = w.S, w.K, w.H, w.E, w.P, w.C
     x_s = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
@@ -810,8 +820,11 @@ def test_step_replays_from_a_captured_graph(moe):
         eo_s.copy_(bf16_dev(f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))))
 
     def step():
-        moe.moe_layout(idx_s, E, P, C, out=lay_s)
-        moe.moe_dispatch(x_s, lay_s.slot_idx, win_s, 0)
+        if fused:
+            moe.moe_layout_dispatch(idx_s, E, P, C, x_s, win_s, 0, out=lay_s)
+        else:
+            moe.moe_layout(idx_s, E, P, C, out=lay_s)
+            moe.moe_dispatch(x_s, lay_s.slot_idx, win_s, 0)
         moe.moe_combine(eo_s, lay_s.slot_idx, wts_s, y=y_s)
 
     def snapshot():
@@ -843,7 +856,7 @@ def test_step_replays_from_a_captured_graph(moe):
         graph.replay()
         torch.cuda.synchronize()
         got = snapshot()
-        note(f"graph replay seed {seed}")
+        note(f"graph replay seed {seed} fused {fused}")
         for a, b in zip(ref[0], got[0]):
             assert np.array_equal(a, b)
         assert np.array_equal(ref[1], got[1]) and np.array_equal(ref[2], got[2])
