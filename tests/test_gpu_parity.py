@@ -602,6 +602,48 @@ def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
             assert np.all(got.expand_x.cpu().numpy()[n:] == 0xCD)
 
 
+@pytest.mark.parametrize("S,K,E,P,C", [(65536, 2, 64, 8, 4096), (1024, 4, 384, 384, 1024)])
+def test_dedup_at_maximum_tokens_and_ranks(moe, S, K, E, P, C):
+    """S = MOE_MAX_TOKENS with C = MOE_MAX_CHANNELS, then P = MOE_MAX_RANKS (one expert per
+    rank): rank rows, the deduplicated fp8 pack and its expansion against the oracle on a small
+    hidden size."""
+    rng = np.random.default_rng(62)
+    H = 16
+    tab = random_tiny_routing(rng, S, K, E, p_mask=0.1, p_bad=0.01)
+    x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    note(f"dedup at S={S} K={K} E={E} P={P} C={C}")
+    lay, rr, win = dedup_dispatch(moe, x, tab, E, P, C, H, 1)
+    ref_rr, ref_base = oracle.rank_rows(tab, E, P)
+    assert np.array_equal(rr.rank_row_idx.cpu().numpy(), ref_rr)
+    assert np.array_equal(rr.rank_token_base.cpu().numpy(), ref_base)
+    ref = oracle.dispatch_dedup(x, ref_rr, tab, E, P, src_rank=5, quant=1)
+    geo = oracle.slot_geometry(H, 1)
+    rows = win.view(-1, geo.slot_bytes).cpu().numpy()
+    assert np.array_equal(rows[: ref.shape[0], : geo.tail_end], ref)
+    check_expansion(moe, win, rr, lay, x, E, P, H, 1)
+
+
+def test_unpack_padded_at_its_limits(moe):
+    """expert_alignment = MOE_MAX_ALIGNMENT and out_rows = MOE_MAX_OUT_ROWS: with 16 non-empty
+    experts the aligned blocks fill the output exactly; with 17 the last block is cut (flag set)."""
+    rng = np.random.default_rng(63)
+    A, R = 65536, 1048576
+    for E, P in ((16, 4), (17, 17)):
+        S, K, H = 96, 2, 16
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+        idx[: E // K + 1] = np.arange(2 * (E // K + 1), dtype=np.int32).reshape(-1, 2) % E  # every expert used
+        x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+        lay = moe.moe_layout(to_dev(idx), E, P, 3)
+        esb = lay.expert_slot_base.cpu().numpy()
+        assert np.all(np.diff(esb) > 0)
+        note(f"unpack_padded limits E={E} A={A} R={R}")
+        got = run_unpack_padded(moe, lay, x, S, K, H, E, 1, A, R)
+        regions = oracle.dispatch_slots(x, lay.slot_idx.cpu().numpy(), 1, 3)
+        ref = oracle.unpack_padded(regions, esb, H, 1, A, R)
+        assert int(ref[4]) == (1 if E * A > R else 0)
+        assert_padded_equal(got, ref, f"limits E={E}")
+
+
 # ---------------------------------------------------------------- combine
 
 
