@@ -119,13 +119,22 @@ __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
     const int lane = threadIdx.x;
     const int v = q * kPartThreads + lane;
     int64_t s = -1;
-    if (r < row_base[E]) {
-        int lo = 0, hi = E;  // largest e with row_base[e] <= r
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (row_base[mid] <= r) lo = mid;
-            else hi = mid;
-        }
+    // The expert of output row r is the largest e < E with row_base[e] <= r. row_base is
+    // non-decreasing, so that e is the number of such entries minus one: the wave loads its lanes'
+    // share of the table in one round of independent loads and counts with ballots; the expert's
+    // three values are then uniform scalar loads. Measured at S=4096, H=7168, A=16: 184 us, against
+    // 188 us for a binary search (a chain of up to nine dependent scalar loads), 208 us for a
+    // two-round vector lookup and 222 us with esb prefetched for every expert.
+    const int total = row_base[E];
+    int count = 0;
+#pragma unroll
+    for (int i = 0; i < (MOE_MAX_EXPERTS + kPartThreads - 1) / kPartThreads; ++i) {
+        const int e = i * kPartThreads + lane;
+        const int base = row_base[min(e, E)];  // row_base holds E + 1 entries
+        count += __popcll(__ballot(e < E && base <= r));
+    }
+    if (r < total) {
+        const int lo = count - 1;  // >= 0: row_base[0] = 0 <= r
         const int64_t j = r - row_base[lo];
         if (j < (int64_t)esb[lo + 1] - esb[lo]) s = esb[lo] + j;
         if (s >= max_slots) s = -1;  // a corrupt base table never reads past the window
