@@ -806,6 +806,47 @@ def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
     assert np.array_equal(y0, y1)
 
 
+def test_two_streams_at_once(moe):
+    """Two independent steps enqueued on two streams so that their kernels can overlap: workload 2
+    through the one-kernel layout + pack (fp8), workload 1 through the separate calls (bf16). The
+    library keeps no state between calls, so each must match the oracle on its own inputs."""
+    jobs = []
+    for cfg, quant, fused in ((2, 1, True), (1, 0, False)):
+        w = WORKLOADS[cfg]
+        inp = inputs(cfg)
+        eo_host = expert_out(cfg)
+        jobs.append(dict(w=w, inp=inp, quant=quant, fused=fused, stream=torch.cuda.Stream(), eo_host=eo_host,
+                         idx=to_dev(inp["topk_idx"]), x=bf16_dev(inp["x"]), eo=bf16_dev(eo_host),
+                         wts=to_dev(inp["topk_weights"]),
+                         lay=poisoned_layout(moe, w.S, w.K, w.E, w.P, w.C),
+                         win=torch.full((moe.moe_window_bytes(w.S, w.K, w.H),), POISON, dtype=torch.uint8,
+                                        device=DEV),
+                         y=torch.empty((w.S, w.H), dtype=torch.bfloat16, device=DEV)))
+    torch.cuda.synchronize()
+    note("two streams: cfg2 fused fp8 and cfg1 separate bf16")
+    for rep in range(3):
+        for j in jobs:
+            w = j["w"]
+            with torch.cuda.stream(j["stream"]):
+                if j["fused"]:
+                    moe.moe_layout_dispatch(j["idx"], w.E, w.P, w.C, j["x"], j["win"], j["quant"], 0, out=j["lay"])
+                else:
+                    moe.moe_layout(j["idx"], w.E, w.P, w.C, out=j["lay"])
+                    moe.moe_dispatch(j["x"], j["lay"].slot_idx, j["win"], j["quant"], 0)
+                moe.moe_combine(j["eo"], j["lay"].slot_idx, j["wts"], y=j["y"])
+    torch.cuda.synchronize()
+    for j in jobs:
+        w, inp = j["w"], j["inp"]
+        ref = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)
+        got = {k: v.cpu().numpy() for k, v in j["lay"]._asdict().items()}
+        assert_layout_equal(got, ref, w.name)
+        win = j["win"].cpu().numpy().reshape(w.S * w.K, -1)
+        assert_window_equal(win, oracle.dispatch_slots(inp["x"], ref["slot_idx"], j["quant"], 0),
+                            oracle.slot_geometry(w.H, j["quant"]), w.name)
+        y = j["y"].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(y, oracle.combine(j["eo_host"], ref["slot_idx"], inp["topk_weights"]))
+
+
 def test_maximum_tokens_and_channels(moe):
     """S = MOE_MAX_TOKENS (65536) with C = MOE_MAX_CHANNELS (4096): layout, dispatch and combine
     against the oracle on a small hidden size."""
