@@ -448,6 +448,8 @@ __global__ __launch_bounds__(kThreads) void layout_pack_small_kernel(
 // round (at 384 workgroups the kernel took twice as long as at 256), although HIP's occupancy
 // calculator reports room for two of these workgroups per unit.
 int compute_units(hipStream_t stream) {
+    // Racing first calls on several host threads all store the same value, so the plain array is
+    // enough; a device id of 64 or more is queried on every call.
     static int cached[64];
     int dev = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess) return 256;
