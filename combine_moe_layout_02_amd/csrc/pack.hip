@@ -18,7 +18,9 @@
 // scale -> narrow; the page's narrow type is INT8, E4M3FN is the second format) needs the whole
 // row's maximum before any code is known, so one workgroup owns one token: each lane holds 16
 // elements (one 16-byte vector of codes), the row max is a wave shuffle reduction followed by an
-// LDS reduction across waves, then codes are written to the K slots.
+// LDS reduction across waves, then codes are written to the K slots. The arithmetic (the correctly
+// rounded quotient by a reciprocal and two FMA corrections, the hardware E4M3 convert) and the
+// slot stores are in pack_rows.h, shared with the fused small-table layout + pack.
 //
 // The deduplicated variants (DeepEP's one copy per destination rank, "Ascend DeepEP MoE Dispatch
 // Optimization", section "一条 token 如何走完 MoE") keep the same workgroup shapes and store each row
