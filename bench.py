@@ -56,6 +56,22 @@ def algorithmic_bytes(w, C, n_valid):
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
+def code_digest(names):
+    """sha256 of the kernel sources `names` (files under combine_moe_layout_02_amd/csrc, in order)
+    with their comments removed, so that an edit to a comment does not retire the counters."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
+    return h.hexdigest()
+
+
 def traffic_from_profiles(kernel_key):
     """HBM bytes per launch from committed rocprofv3 PMC summaries, if still current."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -67,13 +83,7 @@ def traffic_from_profiles(kernel_key):
         rec = data.get(kernel_key)
         if not rec:
             return None
-        import hashlib
-
-        h = hashlib.sha256()
-        for name in rec["sources"]:  # the kernel's file and the headers it includes
-            with open(os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", name), "rb") as f:
-                h.update(f.read())
-        if h.hexdigest() != rec["sources_sha256"]:
+        if code_digest(rec["sources"]) != rec["code_sha256"]:
             return None  # the kernel changed since the counters were taken
         return rec["bytes_per_launch"]
     except (OSError, KeyError, ValueError):

@@ -37,3 +37,18 @@ def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_code_digest_ignores_comments_only(tmp_path, monkeypatch):
+    """The PMC traffic entries are tied to the kernel code, not to its comments."""
+    import bench
+
+    csrc = tmp_path / "combine_moe_layout_02_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (csrc / "k.hip").write_text("// header\nint f() { return 1; }  // trailing\n/* block\n comment */\n")
+    a = bench.code_digest(["k.hip"])
+    (csrc / "k.hip").write_text("// a different header\n\nint f() { return 1; }\n")
+    assert bench.code_digest(["k.hip"]) == a
+    (csrc / "k.hip").write_text("int f() { return 2; }\n")
+    assert bench.code_digest(["k.hip"]) != a
