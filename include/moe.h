@@ -12,9 +12,10 @@
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers; sizes are element counts unless named *_bytes.
  *   - All arrays are dense and row-major.
- *   - The caller allocates and owns every buffer; the library allocates nothing, keeps no state
- *     between calls, and is reentrant. Calls that take a stream only enqueue work on it and return
- *     without synchronising the host.
+ *   - The caller allocates and owns every buffer; the library allocates nothing and keeps no
+ *     state between calls beyond a per-device cache of the compute-unit count (which sizes the
+ *     grid of moe_layout_dispatch), and is reentrant. Calls that take a stream only enqueue work
+ *     on it and return without synchronising the host.
  *   - Arguments are validated on the host before any HIP call. On a validation failure nothing is
  *     enqueued and a negative moe_status is returned. MOE_ERR_HIP reports a failed launch.
  */
