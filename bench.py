@@ -15,7 +15,8 @@ extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
 bounds the event timings at decode sizes. extras.graph_replay_fused_layout_dispatch
 does the same with the layout and the pack in one moe_layout_dispatch call (one
-kernel for decode-sized tables).
+kernel for decode-sized tables); at decode sizes extras.graph_replay_16_steps_per_graph
+puts 16 steps in one graph so that the replay's own launch cost is shared.
 
 kernels: event statistics per call (layout, dispatch = the pack, combine) and
 for the sums layout+dispatch and layout+dispatch+combine, each with its bytes,
@@ -149,10 +150,12 @@ def copy_ceiling(torch, dev, mib=1024, iters=10):
     return gbs
 
 
-def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False):
-    """The same step captured once per input set in a HIP graph and replayed: the device time of a
-    step without the Python launch overhead, which dominates at decode sizes. fused: the layout and
-    the pack through moe_layout_dispatch (one kernel when S*K <= 4096 and C <= 1024)."""
+def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1):
+    """The same step captured in HIP graphs and replayed: the device time of a step without the
+    Python launch overhead, which dominates at decode sizes. per_graph = 1: one graph per input set,
+    one step per replay; per_graph > 1: that many steps (cycling over the input sets) in one graph,
+    so each replay's own launch cost is shared. fused: the layout and the pack through
+    moe_layout_dispatch (one kernel when S*K <= 4096 and C <= 1024)."""
     def step(x, topk, wts, eo):
         if fused:
             moe.moe_layout_dispatch(topk, w.E, w.P, C, x, window, w.quant, 0, out=lay)
@@ -164,12 +167,16 @@ def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
     graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    for x, topk, wts, eo in sets:
+    groups = [[sets[i % len(sets)]] for i in range(len(sets))] if per_graph == 1 else \
+        [[sets[i % len(sets)] for i in range(per_graph)]]
+    for group in groups:
         with torch.cuda.stream(side):  # warm-up on the capture stream
-            step(x, topk, wts, eo)
+            for x, topk, wts, eo in group:
+                step(x, topk, wts, eo)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            step(x, topk, wts, eo)
+            for x, topk, wts, eo in group:
+                step(x, topk, wts, eo)
         graphs.append(g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
@@ -177,13 +184,14 @@ def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
         graphs[i % len(graphs)].replay()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    replays = max(1, args.steps // per_graph)
     torch.cuda.synchronize()
     e0.record()
-    for i in range(args.steps):
+    for i in range(replays):
         graphs[i % len(graphs)].replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / (replays * per_graph)
     del graphs
     return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
@@ -470,6 +478,12 @@ def main():
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
         fused["one_kernel_layout_dispatch"] = w.S * w.K <= 4096 and C <= 1024
         out["extras"]["graph_replay_fused_layout_dispatch"] = fused
+        if w.S * w.K <= 4096:  # decode sizes: 16 steps per graph, the replay's own cost shared
+            out["extras"]["graph_replay_16_steps_per_graph"] = {
+                "separate": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
+                                              per_graph=16),
+                "fused_layout_dispatch": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
+                                                           total_bytes, fused=True, per_graph=16)}
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],
