@@ -766,6 +766,31 @@ def test_combine_from_window_round_trip(moe):
     assert np.all(np.abs(oracle.bf16_bits_to_f32(got) - xr) <= np.abs(xr) * 2.0**-7)
 
 
+def test_combine_row_stride_and_expert_rows(moe):
+    """Rows at a caller stride wider than 2H (here 2H + 528 bytes, filled with garbage between the
+    rows), and expert_rows below the slot count: entries naming a row at or past expert_rows are
+    skipped like pads, so y equals the oracle's combine with those entries set to -1."""
+    rng = np.random.default_rng(71)
+    S, K, H, E, P = 300, 6, 1040, 24, 4
+    idx = random_tiny_routing(rng, S, K, E, p_mask=0.1)
+    slot = oracle.layout(idx, E, P, 5)["slot_idx"]
+    n = int((slot >= 0).sum())
+    rows = f32_to_bf16_input(rng.standard_normal((n, H)).astype(np.float32))
+    wts = rng.random((S, K)).astype(np.float32)
+    stride = 2 * H + 528
+    buf = rng.integers(0, 256, size=(n, stride), dtype=np.uint8)
+    buf[:, : 2 * H] = rows.view(np.uint8).reshape(n, 2 * H)
+    dev_buf = to_dev(buf.reshape(-1))
+    for expert_rows in (n, n // 2, 0):
+        note(f"combine stride {stride} expert_rows {expert_rows} of {n}")
+        y = moe.moe_combine(dev_buf, to_dev(slot), to_dev(wts), row_stride_bytes=stride,
+                            expert_rows=expert_rows, hidden=H)
+        torch.cuda.synchronize()
+        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = oracle.combine(rows, np.where(slot < expert_rows, slot, -1), wts)
+        assert np.array_equal(got, ref), expert_rows
+
+
 # ---------------------------------------------------------------- determinism
 
 
