@@ -368,6 +368,25 @@ def test_dispatch_quant_every_bf16_value(moe, quant):
                         oracle.slot_geometry(H, quant), f"every bf16 quant {quant}")
 
 
+@pytest.mark.parametrize("quant", [0, 1, 2])
+def test_dispatch_any_slot_table(moe, quant):
+    """moe_dispatch takes any table of distinct slots, not only a layout's: a random permutation of
+    [0, N) over the valid entries, with -1 pads and entries at or past S*K, which are skipped."""
+    rng = np.random.default_rng(81 + quant)
+    S, K, H = 150, 5, 2064
+    slot = np.full((S, K), -1, np.int32)
+    keep = rng.random((S, K)) < 0.8
+    n = int(keep.sum())
+    slot[keep] = rng.permutation(n).astype(np.int32)
+    far = (~keep) & (rng.random((S, K)) < 0.5)
+    slot[far] = S * K + rng.integers(0, 1000, int(far.sum())).astype(np.int32)
+    x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32) * 3)
+    note(f"dispatch permuted slots quant {quant}: {n} used, {int(far.sum())} out of range")
+    win = gpu_dispatch(moe, x, slot, quant, src_rank=9)
+    ref = oracle.dispatch_slots(x, np.where(slot < S * K, slot, -1), quant, 9)
+    assert_window_equal(win, ref, oracle.slot_geometry(H, quant), f"permuted quant {quant}")
+
+
 def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
