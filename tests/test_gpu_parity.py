@@ -765,6 +765,32 @@ def test_two_pass_combine_masked_and_partial(moe):
     assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), oracle.combine(rows, slot, wts))
 
 
+def test_combine_scatter_skips_out_of_range_triples(moe):
+    """Rows inside [0, N) whose triple names a token or k outside [0, S) x [0, K) (or negative) are
+    not moved; the others land at row t*K + k."""
+    rng = np.random.default_rng(45)
+    S, K, H = 40, 4, 64
+    n = S * K
+    rows = f32_to_bf16_input(rng.standard_normal((n, H)).astype(np.float32))
+    idx = np.stack([np.zeros(n), np.repeat(np.arange(S), K), np.tile(np.arange(K), S)], axis=1).astype(np.int32)
+    perm = rng.permutation(n)
+    idx = idx[perm]  # rows in a shuffled order
+    bad = rng.choice(n, 25, replace=False)
+    for j, b in enumerate(bad):
+        if j % 2 == 0:
+            idx[b, 1] = (S, -1, S + 7)[j // 2 % 3]  # token out of range
+        else:
+            idx[b, 2] = (K, -1)[j // 2 % 2]  # k out of range
+    staging = torch.full((n, H), -7, dtype=torch.int16, device=DEV)
+    nd = torch.tensor([n], dtype=torch.int32, device=DEV)
+    note("combine_scatter with out-of-range triples")
+    moe.moe_combine_scatter(bf16_dev(rows), to_dev(idx), nd, S, K, staging=staging)
+    torch.cuda.synchronize()
+    ref = oracle.combine_scatter(rows, idx, n, S, K, staging=np.full((n, H), 0xFFF9, np.uint16))
+    assert np.array_equal(staging.cpu().numpy().view(np.uint16), ref)
+    assert (ref == 0xFFF9).all(axis=1).sum() >= 1  # some staging rows received nothing
+
+
 def test_combine_from_window_round_trip(moe):
     """Identity experts: combine read straight from the bf16 window returns x (weights sum to 1)."""
     w = WORKLOADS[3]
