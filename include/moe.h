@@ -166,7 +166,8 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
  *                       fp32(topk_weights[t, k] * fp32(expert_out row slot_idx[t, k])) ),
  * accumulated in fp32 from +0.0, each product and each sum rounded to fp32 (no fused
  * multiply-add), one round-to-nearest-even to bf16 at the end; a token with no valid entry gives
- * +0.0. This is ReadBufferAndWeightedSum of "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 7.8,
+ * +0.0. Infinities and NaNs in the rows or weights propagate as IEEE fp32 arithmetic makes them;
+ * the payload of a NaN result is not specified. This is ReadBufferAndWeightedSum of "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 7.8,
  * with the K rows gathered by slot index instead of first scattered to position t*K + k.
  *
  * In:  expert_out    bf16 rows, row r at byte offset r * row_stride_bytes; 16-byte aligned;
