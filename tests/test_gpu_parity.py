@@ -236,6 +236,8 @@ FUSED_CASES = [
     (128, 16, 16384, 64, 8, 128, 0, 0.0, 0.0, 41),  # largest H and K: row split in 2 parts
     (128, 16, 16384, 64, 8, 128, 2, 0.2, 0.0, 42),
     (200, 3, 4112, 9, 3, 7, 0, 0.0, 0.0, 43),       # ragged channels, H not a multiple of 512 B
+    (256, 4, 2048, 32, 4, 128, 1, 0.1, 0.02, 44),   # S*K = 1024, fp8 with masked and bad ids
+    (205, 5, 2048, 64, 8, 64, 0, 0.1, 0.0, 45),     # odd K, S*K = 1025
     (96, 4, 64, 16, 4, 3, 0, 1.0, 0.0, 44),         # everything masked: nothing written
 ]
 
