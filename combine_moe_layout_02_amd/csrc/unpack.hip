@@ -9,8 +9,8 @@
 //
 // The number of used slots N is read on the device (for example expert_slot_base[E] written by the
 // layout), so no count is read back to the host; the grid covers the worst case S*K and workgroups
-// past N exit at once. Each workgroup owns one (slot, part) of kPartThreads 16-byte vectors: one
-// non-temporal load (the slot is read once) and one streaming store per lane. One-wave parts were
+// past N exit at once. Each workgroup owns one (slot, part) of V 16-byte vectors per lane: V
+// non-temporal loads (the slot is read once) and V streaming stores per lane. One-wave parts were
 // fastest on MI355X at H=7168 (bf16: 146 us against 148 us for 128 lanes; fp8 codes, whose 448
 // vectors split evenly into 64-lane parts but not 128-lane ones: 76 us against 94 us).
 //
@@ -29,6 +29,13 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPartThreads = 64;
+// 16-byte vectors per lane, by kernel (a part is V KB). Measured at S=4096, H=7168 bf16 (fp8):
+// the plain unpack takes 151 (82) us with one vector per lane against 155 (90) us with two; the
+// padded unpack, whose workgroups first look up their row's expert, 172 (98) us with two against
+// 182 (103) us with one and 182 (102) us with four.
+constexpr int kVecsUnpack = 1;
+constexpr int kVecsPadded = 2;
+constexpr int kVecsExpand = 1;
 constexpr int kLoadPolicy = 2;             // nt
 constexpr int kStorePolicy = 1 | 16 | 2;   // sc0 sc1 nt
 
@@ -36,8 +43,10 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// grid = max_slots * nparts; workgroup (s, q) copies vectors [q*kPartThreads, (q+1)*kPartThreads)
-// of slot s's payload to row s; lane 0 of the last part also moves the triple and the scale.
+// grid = max_slots * nparts; workgroup (s, q) copies vectors [q*V*64, (q+1)*V*64) of slot s's
+// payload to row s (vector (q*V + i)*64 + lane in lane's i-th load); lane 0 of the last part also
+// moves the triple and the scale.
+template <int V>
 __global__ __launch_bounds__(kPartThreads) void unpack_kernel(
     const uint8_t *__restrict__ window, const int32_t *__restrict__ num_slots, int max_slots,
     int nparts, SlotGeom g, bool quantised, uint8_t *__restrict__ expand_x,
@@ -45,17 +54,21 @@ __global__ __launch_bounds__(kPartThreads) void unpack_kernel(
     const int s = blockIdx.x / nparts;
     const int q = blockIdx.x - s * nparts;
     const int lane = threadIdx.x;
-    const int v = q * kPartThreads + lane;
     const __amdgpu_buffer_rsrc_t src = rsrc(window + (int64_t)s * g.slot_bytes, g.tail_end);
-    // the load is issued before N arrives: slot s < max_slots always lies inside the window
-    const bool in_row = (v << 4) < g.payload_bytes;
-    const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(src, in_row ? v << 4 : 0, 0, kLoadPolicy);
+    // the loads are issued before N arrives: slot s < max_slots always lies inside the window
+    u32x4 d[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        d[i] = __builtin_amdgcn_raw_buffer_load_b128(src, off < g.payload_bytes ? off : 0, 0, kLoadPolicy);
+    }
     const int n = min(*num_slots, max_slots);
     if (s >= n) return;
-    if (in_row) {
-        const __amdgpu_buffer_rsrc_t dst =
-            rsrc(expand_x + (int64_t)s * g.payload_bytes, g.payload_bytes);
-        __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
+    const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + (int64_t)s * g.payload_bytes, g.payload_bytes);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        if (off < g.payload_bytes) __builtin_amdgcn_raw_buffer_store_b128(d[i], dst, off, 0, kStorePolicy);
     }
     if (q == nparts - 1 && lane == 0) {
         const u32x4 tr = __builtin_amdgcn_raw_buffer_load_b128(src, g.triple_off, 0, kLoadPolicy);
@@ -105,10 +118,11 @@ __global__ __launch_bounds__(kBaseThreads) void unpack_row_base_kernel(
     }
 }
 
-// grid = out_rows * nparts; workgroup (r, q) writes vectors [q*kPartThreads, (q+1)*kPartThreads)
-// of output row r: the part of its source slot's payload, or zeros for a padding row. Lane 0 of
+// grid = out_rows * nparts; workgroup (r, q) writes vectors [q*V*64, (q+1)*V*64) of output row
+// r: the part of its source slot's payload, or zeros for a padding row. Lane 0 of
 // the last part writes the triple and the scale (-1s and 0 for padding). The row's expert is
 // found by a binary search over row_base (E + 1 values, uniform per workgroup).
+template <int V>
 __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
     const uint8_t *__restrict__ window, const int32_t *__restrict__ esb,
     const int32_t *__restrict__ row_base, int E, int64_t max_slots, int nparts, SlotGeom g,
@@ -117,7 +131,6 @@ __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
     const int64_t r = blockIdx.x / nparts;
     const int q = blockIdx.x - (int)(r * nparts);
     const int lane = threadIdx.x;
-    const int v = q * kPartThreads + lane;
     int64_t s = -1;
     // The expert of output row r is the largest e < E with row_base[e] <= r. row_base is
     // non-decreasing, so that e is the number of such entries minus one: the wave loads its lanes'
@@ -139,16 +152,21 @@ __global__ __launch_bounds__(kPartThreads) void unpack_padded_kernel(
         if (j < (int64_t)esb[lo + 1] - esb[lo]) s = esb[lo] + j;
         if (s >= max_slots) s = -1;  // a corrupt base table never reads past the window
     }
-    const bool in_row = (v << 4) < g.payload_bytes;
-    u32x4 d = {0u, 0u, 0u, 0u};
+    u32x4 d[V];
     __amdgpu_buffer_rsrc_t src = rsrc(window, 0);
-    if (s >= 0) {
-        src = rsrc(window + s * g.slot_bytes, g.tail_end);
-        if (in_row) d = __builtin_amdgcn_raw_buffer_load_b128(src, v << 4, 0, kLoadPolicy);
+    if (s >= 0) src = rsrc(window + s * g.slot_bytes, g.tail_end);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        d[i] = u32x4{0u, 0u, 0u, 0u};
+        if (s >= 0 && off < g.payload_bytes)
+            d[i] = __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, kLoadPolicy);
     }
-    if (in_row) {
-        const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + r * g.payload_bytes, g.payload_bytes);
-        __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
+    const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + r * g.payload_bytes, g.payload_bytes);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        if (off < g.payload_bytes) __builtin_amdgcn_raw_buffer_store_b128(d[i], dst, off, 0, kStorePolicy);
     }
     if (q == nparts - 1 && lane == 0) {
         int32_t *idx = expand_idx + r * 3;
@@ -193,6 +211,7 @@ __global__ __launch_bounds__(256) void expand_index_kernel(const int32_t *__rest
     expand_idx[s * 3 + 2] = (int32_t)(i % K);
 }
 
+template <int V>
 __global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
     const uint8_t *__restrict__ window, const int32_t *__restrict__ rank_row_idx,
     const int32_t *__restrict__ num_slots, int S, int K, int64_t max_rows, int64_t max_slots,
@@ -201,7 +220,6 @@ __global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
     const int64_t s = blockIdx.x / nparts;
     const int q = blockIdx.x - (int)(s * nparts);
     const int lane = threadIdx.x;
-    const int v = q * kPartThreads + lane;
     const int64_t n = min((int64_t)*num_slots, max_slots);
     if (s >= n) return;
     const int t = expand_idx[s * 3 + 1], k = expand_idx[s * 3 + 2];
@@ -209,10 +227,17 @@ __global__ __launch_bounds__(kPartThreads) void expand_rows_kernel(
     const int64_t j = rank_row_idx[(int64_t)t * K + k];
     if (j < 0 || j >= max_rows) return;
     const __amdgpu_buffer_rsrc_t src = rsrc(window + j * g.slot_bytes, g.tail_end);
-    if ((v << 4) < g.payload_bytes) {
-        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(src, v << 4, 0, kLoadPolicy);
-        const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + s * g.payload_bytes, g.payload_bytes);
-        __builtin_amdgcn_raw_buffer_store_b128(d, dst, v << 4, 0, kStorePolicy);
+    u32x4 d[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        d[i] = __builtin_amdgcn_raw_buffer_load_b128(src, off < g.payload_bytes ? off : 0, 0, kLoadPolicy);
+    }
+    const __amdgpu_buffer_rsrc_t dst = rsrc(expand_x + s * g.payload_bytes, g.payload_bytes);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int off = ((q * V + i) * kPartThreads + lane) << 4;
+        if (off < g.payload_bytes) __builtin_amdgcn_raw_buffer_store_b128(d[i], dst, off, 0, kStorePolicy);
     }
     if (q == nparts - 1 && lane == 0) {
         expand_idx[s * 3] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(src, g.triple_off, 0, kLoadPolicy);
@@ -235,8 +260,8 @@ hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int nvec = g.payload_bytes / 16;
-    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
-    hipLaunchKernelGGL(expand_rows_kernel, dim3((uint32_t)(n_entries * nparts)), dim3(kPartThreads),
+    const int nparts = (nvec + kVecsExpand * kPartThreads - 1) / (kVecsExpand * kPartThreads);
+    hipLaunchKernelGGL(expand_rows_kernel<kVecsExpand>, dim3((uint32_t)(n_entries * nparts)), dim3(kPartThreads),
                        0, stream, static_cast<const uint8_t *>(window), rank_row_idx, num_slots, S,
                        K, (int64_t)S * (K < P ? K : P), n_entries, nparts, g,
                        quant != MOE_QUANT_NONE, static_cast<uint8_t *>(expand_x), expand_scales,
@@ -255,8 +280,8 @@ hipError_t launch_unpack_padded(const void *window, const int32_t *expert_slot_b
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int nvec = g.payload_bytes / 16;
-    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
-    hipLaunchKernelGGL(unpack_padded_kernel, dim3((uint32_t)(out_rows * nparts)),
+    const int nparts = (nvec + kVecsPadded * kPartThreads - 1) / (kVecsPadded * kPartThreads);
+    hipLaunchKernelGGL(unpack_padded_kernel<kVecsPadded>, dim3((uint32_t)(out_rows * nparts)),
                        dim3(kPartThreads), 0, stream, static_cast<const uint8_t *>(window),
                        expert_slot_base, expert_row_base, E, (int64_t)S * K, nparts, g,
                        quant != MOE_QUANT_NONE, static_cast<uint8_t *>(expand_x), expand_scales,
@@ -270,8 +295,8 @@ hipError_t launch_unpack(const void *window, const int32_t *num_slots, int32_t S
     const SlotGeom g = slot_geom(H, quant);
     const int max_slots = S * K;
     const int nvec = g.payload_bytes / 16;
-    const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
-    hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)max_slots * nparts), dim3(kPartThreads), 0,
+    const int nparts = (nvec + kVecsUnpack * kPartThreads - 1) / (kVecsUnpack * kPartThreads);
+    hipLaunchKernelGGL(unpack_kernel<kVecsUnpack>, dim3((uint32_t)max_slots * nparts), dim3(kPartThreads), 0,
                        stream, static_cast<const uint8_t *>(window), num_slots, max_slots, nparts,
                        g, quant != MOE_QUANT_NONE, static_cast<uint8_t *>(expand_x), expand_scales,
                        expand_idx);
