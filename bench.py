@@ -18,9 +18,15 @@ does the same with the layout and the pack in one moe_layout_dispatch call (one
 kernel for decode-sized tables); at decode sizes extras.graph_replay_16_steps_per_graph
 puts 16 steps in one graph so that the replay's own launch cost is shared.
 
-kernels: event statistics per call (layout, dispatch = the pack, combine) and
+Timing: value and ms_per_step come from the K timed steps with nothing recorded
+between the kernels (wall clock between two device synchronisations). The same
+K steps then run again with an event before and after every kernel; kernels
+holds those event statistics per call (layout, dispatch = the pack, combine) and
 for the sums layout+dispatch and layout+dispatch+combine, each with its bytes,
 GB/s, fraction of 8 TB/s, tokens/s and fraction of the measured copy ceiling.
+Each event adds a few microseconds to the interval it bounds, so the event
+figures are upper bounds on the kernel durations; ms_per_step_with_events is the
+step time of that second pass.
 
 Algorithmic bytes (what the method must move; zero padding and the window
 reservation are not traffic):
@@ -380,18 +386,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def step(i, sets_used):
+        x, topk, wts, eo = sets_used[i % len(sets_used)]
+        moe.moe_layout(topk, w.E, w.P, C, out=lay)
+        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
     def timed(sets_used):
-        """W untimed then K timed steps cycling over sets_used: per-kernel event statistics and the
-        wall time per step between two device synchronisations."""
+        """W untimed then K timed steps cycling over sets_used, timed by the wall clock between two
+        device synchronisations with nothing recorded between the kernels; then the same K steps
+        again with an event between every two kernels for the per-kernel statistics (each event
+        adds a few microseconds to the step, so that pass is not the step time)."""
         for i in range(args.warmup):
-            x, topk, wts, eo = sets_used[i % len(sets_used)]
-            moe.moe_layout(topk, w.E, w.P, C, out=lay)
-            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
-            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+            step(i, sets_used)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, sets_used)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
         for i in range(args.steps):
             e = ev[i]
             x, topk, wts, eo = sets_used[i % len(sets_used)]
@@ -403,7 +419,7 @@ def main():
             moe.moe_combine(eo, lay.slot_idx, wts, y=y)
             e[3].record(stream)
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        elapsed_events = time.perf_counter() - t1
         ms = {k: [] for k in ("layout", "dispatch", "combine")}
         for e in ev:
             ms["layout"].append(e[0].elapsed_time(e[1]))
@@ -426,11 +442,11 @@ def main():
             }
             if copy_gbs:
                 kernels[k]["frac_copy_ceiling"] = round(gbs / copy_gbs, 4)
-        return kernels, 1e3 * elapsed / args.steps
+        return kernels, 1e3 * elapsed / args.steps, 1e3 * elapsed_events / args.steps
 
     nbytes = algorithmic_bytes(w, C, n_valid)
     copy_gbs = None if args.no_extras else copy_ceiling(torch, dev)
-    kernels, ms_per_step = timed(sets)
+    kernels, ms_per_step, ms_per_step_events = timed(sets)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
@@ -462,6 +478,7 @@ def main():
                    "parallelism": "single GPU (P virtual ranks)"},
         "tokens_per_s": round(w.S / (ms_per_step * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_with_events": round(ms_per_step_events, 4),
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
@@ -469,7 +486,7 @@ def main():
     if not args.no_extras:
         out["extras"] = {"copy_ceiling_GB/s": round(copy_gbs, 1), "copy_method": "torch copy_ (hipMemcpyAsync device to device) of 1 GiB, read+write bytes"}
         if len(sets) > 1:
-            warm, warm_ms = timed(sets[:1])
+            warm, warm_ms, _ = timed(sets[:1])
             out["extras"]["warm_same_buffers"] = {
                 "value": round(total_bytes / (warm_ms * 1e-3) / 1e9, 1), "ms_per_step": round(warm_ms, 4),
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
