@@ -105,10 +105,18 @@ def cpu_baseline(w, C, inp, expert_out, n_valid, min_seconds=10.0, max_reps=25):
     ru0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
     reps = 0
+    stage_s = {"layout": 0.0, "dispatch": 0.0, "combine": 0.0}
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        ta = time.perf_counter()
         lay = oracle.layout(inp["topk_idx"], w.E, w.P, C)
+        tb = time.perf_counter()
         oracle.dispatch_slots(inp["x"], lay["slot_idx"], w.quant, 0)
+        tc = time.perf_counter()
         oracle.combine(expert_out, lay["slot_idx"], inp["topk_weights"])
+        td = time.perf_counter()
+        stage_s["layout"] += tb - ta
+        stage_s["dispatch"] += tc - tb
+        stage_s["combine"] += td - tc
         reps += 1
     wall = time.perf_counter() - t0
     ru1 = resource.getrusage(resource.RUSAGE_SELF)
@@ -122,6 +130,7 @@ def cpu_baseline(w, C, inp, expert_out, n_valid, min_seconds=10.0, max_reps=25):
         "sample": f"{reps} full steps (layout+dispatch+combine) of {w.describe()}, {wall:.1f} s wall, "
                   f"{cpu:.1f} s cpu, {reps * w.S / wall:.0f} tokens/s; numpy on one thread; host has "
                   f"{os.cpu_count()} logical cpus ({cpu_model()})",
+        "stage_ms": {k: round(1e3 * v / reps, 3) for k, v in stage_s.items()},
     }
 
 

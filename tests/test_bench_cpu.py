@@ -52,3 +52,17 @@ def test_code_digest_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.code_digest(["k.hip"]) == a
     (csrc / "k.hip").write_text("int f() { return 2; }\n")
     assert bench.code_digest(["k.hip"]) != a
+
+
+def test_cpu_baseline_fields():
+    """The oracle leg of the bench on the tiny workload: one full step, its stages timed apart."""
+    from workloads import make_inputs
+
+    w = WORKLOADS[1]
+    inp = make_inputs(w)
+    n_valid = int(((inp["topk_idx"] >= 0) & (inp["topk_idx"] < w.E)).sum())
+    cb = bench.cpu_baseline(w, w.C, inp, inp["expert_out"], n_valid, min_seconds=0.0, max_reps=1)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] >= 1 and cb["value"] > 0
+    assert set(cb["stage_ms"]) == {"layout", "dispatch", "combine"}
+    assert all(v >= 0 for v in cb["stage_ms"].values())
+    assert cb["sample"].startswith("1 full steps")
