@@ -326,6 +326,45 @@ def test_dispatch_tiny(moe, case):
                         oracle.slot_geometry(H, quant), str(case))
 
 
+LARGE_DISPATCH = [
+    # (S, K, H, E, P, p_mask, seed): bf16 windows of 16k+ slots with rows of 4096+ elements
+    (2100, 8, 4096, 64, 8, 0.1, 91),
+    (2300, 8, 7200, 40, 8, 0.05, 92),    # 900 vectors per row: a ragged last part
+    (2049, 8, 16384, 256, 8, 0.0, 93),   # MOE_MAX_HIDDEN
+    (1100, 16, 7168, 128, 16, 0.2, 94),  # K at its maximum
+    (3001, 6, 4112, 48, 4, 0.1, 95),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_DISPATCH)
+def test_dispatch_large_shapes(moe, case):
+    S, K, H, E, P, p_mask, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32) * 2)
+    slot = oracle.layout(idx, E, P, min(S, 128))["slot_idx"]
+    note(f"dispatch large {case}")
+    win = gpu_dispatch(moe, xb, slot, 0, src_rank=seed)
+    assert_window_equal(win, oracle.dispatch_slots(xb, slot, 0, seed), oracle.slot_geometry(H, 0), str(case))
+
+
+def test_dispatch_large_any_slot_table(moe):
+    """A random permutation of the slots of a 16k-slot window, -1 pads and entries past S*K."""
+    rng = np.random.default_rng(96)
+    S, K, H = 2048, 8, 4096
+    slot = np.full((S, K), -1, np.int32)
+    keep = rng.random((S, K)) < 0.9
+    n = int(keep.sum())
+    slot[keep] = rng.permutation(n).astype(np.int32)
+    far = (~keep) & (rng.random((S, K)) < 0.5)
+    slot[far] = S * K + rng.integers(0, 1000, int(far.sum())).astype(np.int32)
+    x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    note(f"dispatch large permuted slots: {n} used, {int(far.sum())} out of range")
+    win = gpu_dispatch(moe, x, slot, 0, src_rank=4)
+    ref = oracle.dispatch_slots(x, np.where(slot < S * K, slot, -1), 0, 4)
+    assert_window_equal(win, ref, oracle.slot_geometry(H, 0), "large permuted")
+
+
 def every_bf16_rows(amax_bits, H):
     """Rows that pass every finite bf16 value of magnitude <= amax through the quantiser with the
     row maximum amax: per amax, element 0 of each row is +-amax and the rest of the rows hold all
