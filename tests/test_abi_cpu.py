@@ -42,6 +42,19 @@ def test_slot_geometry_matches_golden():
     assert moe.moe_window_bytes(4096, 8, 7168) == 4096 * 8 * 14848
 
 
+def test_slot_geometry_every_hidden_size():
+    """The library's slot arithmetic against the oracle's for every accepted H and every mode."""
+    import oracle
+
+    for H in range(16, 16384 + 1, 16):
+        assert moe.moe_slot_bytes(H) == oracle.slot_geometry(H, 0).slot_bytes
+        for q in (0, 1, 2):
+            geo = oracle.slot_geometry(H, q)
+            assert moe.moe_slot_offsets(H, q) == dict(
+                payload_bytes=geo.payload_bytes, scale_off=geo.scale_off, triple_off=geo.triple_off,
+                tail_end=geo.tail_end), (H, q)
+
+
 @pytest.mark.parametrize("H,err", [(0, -1), (8, -1), (1000, -4), (16400, -1), (32768, -1)])
 def test_bad_hidden(H, err):
     assert moe._lib.moe_slot_bytes(H) == err
