@@ -95,14 +95,21 @@ def _check(status):
     raise ValueError(msg)
 
 
+# The raw handle of the current stream without building a torch Stream object (about 2 us per
+# call less); torch.cuda.current_stream is the fallback where that accessor is missing.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(dev, stream):
     if stream is not None:
-        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _need(t, name, dtype=None, ndim=None, device=None):
@@ -118,6 +125,18 @@ def _need(t, name, dtype=None, ndim=None, device=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _need_layout(out, S, K, E, P, C, dev):
+    """The nine Layout buffers: device, dtype, shape and contiguity."""
+    shapes = ((S, P), (P,), (E,), (P, C), (E, C), (P + 1,), (E + 1,), (S, K), (1,))
+    for i, (t, shp) in enumerate(zip(out, shapes)):
+        dtype = torch.bool if i == 0 else torch.int32
+        if (not isinstance(t, torch.Tensor) or t.device != dev or t.dtype != dtype
+                or t.shape != shp or not t.is_contiguous()):
+            name = Layout._fields[i]
+            _need(t, name, dtype, device=dev)
+            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
 
 
 def moe_slot_bytes(H):
@@ -172,11 +191,7 @@ def moe_layout(topk_idx, num_experts, num_ranks, num_channels, out=None, stream=
     dev = topk_idx.device
     if out is None:
         out = empty_layout(S, K, E, P, C, dev)
-    shapes = [(S, P), (P,), (E,), (P, C), (E, C), (P + 1,), (E + 1,), (S, K), (1,)]
-    for name, t, shp in zip(Layout._fields, out, shapes):
-        _need(t, name, torch.bool if name == "is_token_in_rank" else torch.int32, device=dev)
-        if tuple(t.shape) != shp:
-            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+    _need_layout(out, S, K, E, P, C, dev)
     _check(_lib.moe_layout(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
                            _stream(dev, stream)))
     return out
@@ -211,11 +226,7 @@ def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, windo
     E, P, C = int(num_experts), int(num_ranks), int(num_channels)
     if out is None:
         out = empty_layout(S, K, E, P, C, dev)
-    shapes = [(S, P), (P,), (E,), (P, C), (E, C), (P + 1,), (E + 1,), (S, K), (1,)]
-    for name, t, shp in zip(Layout._fields, out, shapes):
-        _need(t, name, torch.bool if name == "is_token_in_rank" else torch.int32, device=dev)
-        if tuple(t.shape) != shp:
-            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+    _need_layout(out, S, K, E, P, C, dev)
     nbytes = window.numel() * window.element_size()
     _check(_lib.moe_layout_dispatch(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
                                     _ptr(x), H, int(quant), int(src_rank), _ptr(window), nbytes,
