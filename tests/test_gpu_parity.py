@@ -428,6 +428,22 @@ def test_dispatch_any_slot_table(moe, quant):
     assert_window_equal(win, ref, oracle.slot_geometry(H, quant), f"permuted quant {quant}")
 
 
+def test_dispatch_bf16_copies_non_finite_bits(moe):
+    """The bf16 pack is a byte copy: infinities and NaN payloads (quiet and signalling bit
+    patterns) arrive unchanged."""
+    rng = np.random.default_rng(78)
+    S, K, H, E = 40, 4, 512, 8
+    idx = random_tiny_routing(rng, S, K, E, p_mask=0.1)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x7FFF, 0x8000], np.uint16)
+    pick = rng.random((S, H)) < 0.05
+    xb[pick] = rng.choice(specials, size=int(pick.sum()))
+    slot = oracle.layout(idx, E, 2, 1)["slot_idx"]
+    note("dispatch bf16 non-finite bits")
+    win = gpu_dispatch(moe, xb, slot, 0, src_rank=1)
+    assert_window_equal(win, oracle.dispatch_slots(xb, slot, 0, 1), oracle.slot_geometry(H, 0), "non-finite bf16")
+
+
 def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
@@ -743,6 +759,33 @@ def test_combine_tiny(moe, case):
     ref = oracle.combine(rows, slot, w)
     assert_bf16_within_ulp(got, ref, str(case))
     assert np.array_equal(got, ref), f"{case}: within 1 ulp but not bit-exact"
+
+
+def test_combine_non_finite_inputs(moe):
+    """Infinities and NaNs in the rows and the weights: every result that is a number (finite or
+    infinite) matches the oracle's IEEE fp32 reduction bit for bit; every NaN result is a NaN
+    (its payload is not specified). Large finite rows and weights also overflow to infinity."""
+    rng = np.random.default_rng(77)
+    S, K, H, R = 96, 6, 256, 300
+    slot = np.stack([rng.choice(R, size=K, replace=False) for _ in range(S)]).astype(np.int32)
+    slot[rng.random((S, K)) < 0.1] = -1
+    vals = rng.standard_normal((R, H)).astype(np.float32) * 3
+    special = np.array([np.inf, -np.inf, np.nan, 3.0e38, -3.0e38], np.float32)
+    pick = rng.random((R, H)) < 0.02
+    vals[pick] = rng.choice(special, size=int(pick.sum()))
+    rows = f32_to_bf16_input(vals)
+    w = rng.standard_normal((S, K)).astype(np.float32)
+    wpick = rng.random((S, K)) < 0.05
+    w[wpick] = rng.choice(np.array([np.inf, -np.inf, np.nan, 1e30], np.float32), size=int(wpick.sum()))
+    note("combine non-finite inputs")
+    got = gpu_combine(moe, rows, slot, w)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.combine(rows, slot, w)
+    ref_nan = np.isnan(oracle.bf16_bits_to_f32(ref))
+    got_nan = np.isnan(oracle.bf16_bits_to_f32(got))
+    assert ref_nan.any() and np.isinf(oracle.bf16_bits_to_f32(ref)).any(), "the inputs reach NaN and infinity"
+    assert np.array_equal(got_nan, ref_nan), "NaN results differ in position"
+    assert np.array_equal(got[~ref_nan], ref[~ref_nan]), "non-NaN results differ"
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
