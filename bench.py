@@ -11,6 +11,8 @@ Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
 at distinct addresses, so each step reads its inputs from HBM rather than from
 the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); extras.warm_same_buffers repeats the timing with
 one set of buffers. extras.copy_ceiling_GB/s is a 1 GiB device-to-device copy.
+extras.fused_layout_dispatch times the same eager steps with the layout and the pack
+in one moe_layout_dispatch call (one kernel for decode-sized tables).
 extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
 bounds the event timings at decode sizes. extras.graph_replay_fused_layout_dispatch
@@ -163,6 +165,26 @@ def copy_ceiling(torch, dev, mib=1024, iters=10):
     gbs = 2 * n * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     return gbs
+
+
+def time_fused_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
+    """The step with the layout and the pack through moe_layout_dispatch, launched eagerly like the
+    timed steps (W warm-up, K steps between two device synchronisations, nothing in between)."""
+    def step(i):
+        x, topk, wts, eo = sets[i % len(sets)]
+        moe.moe_layout_dispatch(topk, w.E, w.P, C, x, window, w.quant, 0, out=lay)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
 def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1):
@@ -499,6 +521,8 @@ def main():
             out["extras"]["warm_same_buffers"] = {
                 "value": round(total_bytes / (warm_ms * 1e-3) / 1e9, 1), "ms_per_step": round(warm_ms, 4),
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
+        out["extras"]["fused_layout_dispatch"] = time_fused_eager(args, torch, moe, w, C, sets, lay, window,
+                                                                  y, total_bytes)
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                           total_bytes)
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
