@@ -550,10 +550,11 @@ def test_unpack_padded_workloads(moe, cfg, quant):
         assert_padded_equal(got, ref, f"cfg{cfg} A={A} R={R}")
 
 
-def test_unpack_padded_tiny_and_degenerate(moe):
+@pytest.mark.parametrize("H", [48, 2064])  # 2064: 258 bf16 vectors, the last 256-vector part ragged
+def test_unpack_padded_tiny_and_degenerate(moe, H):
     """Masked entries, empty experts, R = 1, alignment larger than every count."""
     rng = np.random.default_rng(33)
-    S, K, E, P, H = 40, 3, 12, 4, 48
+    S, K, E, P = 40, 3, 12, 4
     tab = random_tiny_routing(rng, S, K, E, p_mask=0.3)
     tab[:, :] = np.where(np.isin(tab, [2, 3]), -1, tab)  # experts 2 and 3 receive nothing
     xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
