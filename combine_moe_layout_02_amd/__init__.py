@@ -28,11 +28,15 @@ MOE_QUANT_NONE = 0
 MOE_QUANT_FP8_E4M3_DYN = 1
 MOE_QUANT_INT8_DYN = 2
 
+MOE_LAYOUT_AUTO = 0
+MOE_LAYOUT_MULTI = 1
+MOE_LAYOUT_SINGLE = 2
+
 EXPORTED = (
-    "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_dispatch",
-    "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "moe_unpack_padded",
-    "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup", "moe_expand_dedup",
-    "moe_status_string",
+    "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_layout_ex", "moe_dispatch",
+    "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
+    "moe_unpack", "moe_unpack_padded", "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup",
+    "moe_expand_dedup", "moe_status_string",
 )
 
 
@@ -53,12 +57,15 @@ def _load():
         "moe_window_bytes": (I64, [I32, I32, I32]),
         "moe_slot_offsets": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
+        "moe_layout_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [I32, P]),
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_layout_dispatch": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
                                 [P, I32, I32, I32, P, I64, P]),
+        "moe_layout_dispatch_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
+                                   [P, I32, I32, I32, P, I64, I32, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
         "moe_combine_scatter": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, I64, I64, P]),
-        "moe_combine_staged": (ctypes.c_int, [P, I64, P, P, I32, I32, I32, P, P]),
+        "moe_combine_staged": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
         "moe_unpack": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, P, P, P]),
         "moe_dedup_window_bytes": (I64, [I32, I32, I32, I32]),
         "moe_rank_rows": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P]),
@@ -183,8 +190,9 @@ def empty_layout(S, K, E, P, C, device):
     )
 
 
-def moe_layout(topk_idx, num_experts, num_ranks, num_channels, out=None, stream=None):
-    """Routing layout of topk_idx (int32 [S, K]) for E experts over P ranks and C channels."""
+def moe_layout(topk_idx, num_experts, num_ranks, num_channels, out=None, stream=None, path=None):
+    """Routing layout of topk_idx (int32 [S, K]) for E experts over P ranks and C channels.
+    path: None (moe_layout: the form is chosen by size) or a MOE_LAYOUT_* value (moe_layout_ex)."""
     _need(topk_idx, "topk_idx", torch.int32, 2)
     S, K = topk_idx.shape
     E, P, C = int(num_experts), int(num_ranks), int(num_channels)
@@ -192,8 +200,12 @@ def moe_layout(topk_idx, num_experts, num_ranks, num_channels, out=None, stream=
     if out is None:
         out = empty_layout(S, K, E, P, C, dev)
     _need_layout(out, S, K, E, P, C, dev)
-    _check(_lib.moe_layout(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
-                           _stream(dev, stream)))
+    if path is None:
+        _check(_lib.moe_layout(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                               _stream(dev, stream)))
+    else:
+        _check(_lib.moe_layout_ex(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out], int(path),
+                                  _stream(dev, stream)))
     return out
 
 
@@ -213,8 +225,9 @@ def moe_dispatch(x, slot_idx, window, quant=MOE_QUANT_NONE, src_rank=0, stream=N
 
 
 def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, window,
-                        quant=MOE_QUANT_NONE, src_rank=0, out=None, stream=None):
-    """moe_layout and moe_dispatch in one call (one kernel for small tables); returns the Layout."""
+                        quant=MOE_QUANT_NONE, src_rank=0, out=None, stream=None, path=None):
+    """moe_layout and moe_dispatch in one call (one kernel for small tables); returns the Layout.
+    path: None (moe_layout_dispatch) or a MOE_LAYOUT_* value (moe_layout_dispatch_ex)."""
     _need(topk_idx, "topk_idx", torch.int32, 2)
     dev = topk_idx.device
     _need(x, "x", torch.bfloat16, 2, dev)
@@ -228,9 +241,14 @@ def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, windo
         out = empty_layout(S, K, E, P, C, dev)
     _need_layout(out, S, K, E, P, C, dev)
     nbytes = window.numel() * window.element_size()
-    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
-                                    _ptr(x), H, int(quant), int(src_rank), _ptr(window), nbytes,
-                                    _stream(dev, stream)))
+    if path is None:
+        _check(_lib.moe_layout_dispatch(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                                        _ptr(x), H, int(quant), int(src_rank), _ptr(window), nbytes,
+                                        _stream(dev, stream)))
+    else:
+        _check(_lib.moe_layout_dispatch_ex(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                                           _ptr(x), H, int(quant), int(src_rank), _ptr(window), nbytes,
+                                           int(path), _stream(dev, stream)))
     return out
 
 
@@ -307,15 +325,14 @@ def moe_combine_staged(staging, slot_idx, topk_weights, hidden, staging_stride_b
     stride = 2 * H if staging_stride_bytes is None else int(staging_stride_bytes)
     if tuple(topk_weights.shape) != (S, K):
         raise ValueError("topk_weights must match slot_idx")
-    if ((S * K - 1) * stride + 2 * H) > staging.numel() * staging.element_size():
-        raise ValueError("staging must hold S*K rows of the given stride")
     if y is None:
         y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, 2, dev)
     if tuple(y.shape) != (S, H):
         raise ValueError(f"y must have shape {(S, H)}")
-    _check(_lib.moe_combine_staged(_ptr(staging), stride, _ptr(slot_idx), _ptr(topk_weights), S, H, K,
-                                   _ptr(y), _stream(dev, stream)))
+    _check(_lib.moe_combine_staged(_ptr(staging), stride, staging.numel() * staging.element_size(),
+                                   _ptr(slot_idx), _ptr(topk_weights), S, H, K, _ptr(y),
+                                   _stream(dev, stream)))
     return y
 
 
@@ -505,7 +522,8 @@ def moe_unpack_padded(window, expert_slot_base, S, K, H, quant=MOE_QUANT_NONE, e
 
 __all__ = [
     "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_ALIGN", "MOE_ERR_WINDOW", "MOE_ERR_UNSUPPORTED",
-    "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MoeError", "Layout",
+    "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MOE_LAYOUT_AUTO",
+    "MOE_LAYOUT_MULTI", "MOE_LAYOUT_SINGLE", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
     "moe_dispatch", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",

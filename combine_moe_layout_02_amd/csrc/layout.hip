@@ -412,10 +412,6 @@ hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t 
                          int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                          int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                          hipStream_t stream) {
-    if (layout_small_enabled() && layout_small_fits(S, K, E, P, C))
-        return launch_layout_small(topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
-                                   num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
-                                   rank_slot_base, expert_slot_base, slot_idx, status, stream);
     hipError_t err;
     if (K <= 1)
         err = launch_count<1>(topk_idx, S, K, E, P, C, is_token_in_rank, rank_prefix_matrix, expert_prefix_matrix, slot_idx, stream);

@@ -37,6 +37,8 @@
 //            kernels store it. The layout workgroups write slot_idx from their own counts, so no
 //            workgroup waits for another and the dispatch needs no second launch.
 
+#include <atomic>
+
 #include "pack_rows.h"
 
 namespace moe {
@@ -448,16 +450,19 @@ __global__ __launch_bounds__(kThreads) void layout_pack_small_kernel(
 // round (at 384 workgroups the kernel took twice as long as at 256), although HIP's occupancy
 // calculator reports room for two of these workgroups per unit.
 int compute_units(hipStream_t stream) {
-    // Racing first calls on several host threads all store the same value, so the plain array is
-    // enough; a device id of 64 or more is queried on every call.
-    static int cached[64];
+    // Racing first calls on several host threads all store the same value; relaxed atomics make
+    // that race well defined. A device id of 64 or more is queried on every call.
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev >= 0 && dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
         n = 256;
-    if (dev >= 0 && dev < 64) cached[dev] = n;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

@@ -7,7 +7,6 @@
 // DeepEP Python entry ("Ascend DeepEP MoE Dispatch Optimization", section "从 Python 接口进入真实调用链").
 
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "moe_internal.h"
 
@@ -35,6 +34,19 @@ bool extent_fits(int64_t rows, int64_t stride) {
     return rows <= 1 || stride <= INT64_MAX / rows;
 }
 
+// Which layout form a call takes: -1 for a path value outside moe_layout_path, 1 for the
+// single-launch form, 0 for the multi-launch form. MOE_LAYOUT_SINGLE on a table the single launch
+// cannot take is reported as MOE_ERR_UNSUPPORTED by the caller (returned here as 2).
+int pick_layout(int32_t path, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
+    const bool fits = moe::layout_small_fits(S, K, E, P, C);
+    switch (path) {
+        case MOE_LAYOUT_AUTO: return fits ? 1 : 0;
+        case MOE_LAYOUT_MULTI: return 0;
+        case MOE_LAYOUT_SINGLE: return fits ? 1 : 2;
+        default: return -1;
+    }
+}
+
 int check_experts(int32_t E, int32_t P) {
     if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
     if (E % P != 0) return MOE_ERR_UNSUPPORTED;
@@ -49,11 +61,6 @@ bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
     (void)E;
     (void)P;
     return (int64_t)S * K <= kSmallLayoutEntries && C <= kSmallLayoutChannels;
-}
-
-bool layout_small_enabled() {
-    const char *v = getenv("MOE_LAYOUT_SMALL");
-    return !(v && v[0] == '0');
 }
 
 }  // namespace moe
@@ -96,11 +103,12 @@ int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *
     return MOE_OK;
 }
 
-int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
-               uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
-               int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
-               int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
-               int32_t *slot_idx, int32_t *status, hipStream_t stream) {
+int moe_layout_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                  uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                  int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                  int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                  int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t path,
+                  hipStream_t stream) {
     if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
         !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
         !slot_idx || !status)
@@ -110,14 +118,33 @@ int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t
     if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
     if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
     if (E % P != 0) return MOE_ERR_UNSUPPORTED;
+    const int form = pick_layout(path, S, K, E, P, C);
+    if (form < 0) return MOE_ERR_ARG;
+    if (form == 2) return MOE_ERR_UNSUPPORTED;
     const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
                          expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
     for (const void *p : i32)
         if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+    if (form == 1)
+        return from_hip(moe::launch_layout_small(
+            topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
+            rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
+            status, stream));
     return from_hip(moe::launch_layout(topk_idx, S, K, E, P, C, is_token_in_rank,
                                        num_tokens_per_rank, num_tokens_per_expert,
                                        rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
                                        expert_slot_base, slot_idx, status, stream));
+}
+
+int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+               uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+               int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+               int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
+               int32_t *slot_idx, int32_t *status, hipStream_t stream) {
+    return moe_layout_ex(topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                         num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                         rank_slot_base, expert_slot_base, slot_idx, status, MOE_LAYOUT_AUTO,
+                         stream);
 }
 
 int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
@@ -134,13 +161,13 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
 }
 
-int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
-                        int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
-                        int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
-                        int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
-                        int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
-                        const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
-                        int64_t window_bytes, hipStream_t stream) {
+int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                           int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                           int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                           int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                           int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                           const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                           int64_t window_bytes, int32_t path, hipStream_t stream) {
     if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
         !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
         !slot_idx || !status || !x || !window)
@@ -153,13 +180,16 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
     if (st != MOE_OK) return st;
     if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
     if (E % P != 0) return MOE_ERR_UNSUPPORTED;
+    const int form = pick_layout(path, S, K, E, P, C);
+    if (form < 0) return MOE_ERR_ARG;
+    if (form == 2) return MOE_ERR_UNSUPPORTED;
     const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
                          expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
     for (const void *p : i32)
         if (!aligned(p, 4)) return MOE_ERR_ALIGN;
     if (!aligned(x, 16) || !aligned(window, 512)) return MOE_ERR_ALIGN;
     if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
-    if (moe::layout_small_enabled() && moe::layout_small_fits(S, K, E, P, C))
+    if (form == 1)
         return from_hip(moe::launch_layout_dispatch_small(
             topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
             rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
@@ -170,6 +200,19 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
                                      expert_slot_base, slot_idx, status, stream));
     if (st != MOE_OK) return st;
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+}
+
+int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                        int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                        int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                        int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                        int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                        const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                        int64_t window_bytes, hipStream_t stream) {
+    return moe_layout_dispatch_ex(topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                                  num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                                  rank_slot_base, expert_slot_base, slot_idx, status, x, H, quant,
+                                  src_rank, window, window_bytes, MOE_LAYOUT_AUTO, stream);
 }
 
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
@@ -213,9 +256,9 @@ int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_
                                                 staging_stride_bytes, stream));
 }
 
-int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const int32_t *slot_idx,
-                       const float *topk_weights, int32_t S, int32_t H, int32_t K, void *y,
-                       hipStream_t stream) {
+int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, int64_t staging_bytes,
+                       const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
+                       int32_t K, void *y, hipStream_t stream) {
     if (!staging || !slot_idx || !topk_weights || !y) return MOE_ERR_ARG;
     int st = check_tokens(S, K);
     if (st != MOE_OK) return st;
@@ -225,6 +268,10 @@ int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const 
     if (staging_stride_bytes % 16 != 0 || !aligned(staging, 16) || !aligned(y, 16) ||
         !aligned(slot_idx, 4) || !aligned(topk_weights, 4))
         return MOE_ERR_ALIGN;
+    // staging_bytes >= (S*K - 1) * staging_stride_bytes + 2H, in a form that cannot overflow
+    if (staging_bytes < 2 * (int64_t)H ||
+        (staging_bytes - 2 * (int64_t)H) / staging_stride_bytes < (int64_t)S * K - 1)
+        return MOE_ERR_WINDOW;
     return from_hip(moe::launch_combine_staged(staging, staging_stride_bytes, slot_idx,
                                                topk_weights, S, H, K, y, stream));
 }
@@ -337,7 +384,7 @@ const char *moe_status_string(int status) {
         case MOE_OK: return "ok";
         case MOE_ERR_ARG: return "invalid argument (null pointer or size out of range)";
         case MOE_ERR_ALIGN: return "misaligned pointer or stride";
-        case MOE_ERR_WINDOW: return "window too small: need S*K*moe_slot_bytes(H) bytes";
+        case MOE_ERR_WINDOW: return "buffer too small: the window (S*K*moe_slot_bytes(H) bytes) or staging rows";
         case MOE_ERR_UNSUPPORTED: return "unsupported shape (E % P != 0, H % 16 != 0 or S too large)";
         case MOE_ERR_HIP: return "HIP launch error";
         default: return "unknown status";

@@ -42,11 +42,9 @@ constexpr int kSmallLayoutChannels = 1024;  // C
 // True when the single-launch layout can take (S, K, E, P, C).
 bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C);
 
-// False when MOE_LAYOUT_SMALL=0 is set in the environment (read on every call): then the
-// three-launch layout runs even for small tables.
-bool layout_small_enabled();
-
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
+
+// The multi-launch layout (count per channel, scan along channels, assign), any accepted size.
 hipError_t launch_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                          int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                          int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,

@@ -33,7 +33,8 @@ typedef enum {
     MOE_OK = 0,
     MOE_ERR_ARG = -1,         /* null pointer or a size outside its documented range          */
     MOE_ERR_ALIGN = -2,       /* a pointer or stride is not aligned as documented             */
-    MOE_ERR_WINDOW = -3,      /* window_bytes < moe_window_bytes(S, K, H)                     */
+    MOE_ERR_WINDOW = -3,      /* window_bytes < moe_window_bytes(S, K, H), or a staging buffer
+                                 shorter than its S*K rows                                    */
     MOE_ERR_UNSUPPORTED = -4, /* E % P != 0, H % 16 != 0, or S above MOE_MAX_TOKENS           */
     MOE_ERR_HIP = -5          /* the HIP runtime reported an error for a launch               */
 } moe_status;
@@ -106,14 +107,32 @@ int moe_slot_offsets(int32_t H, int32_t quant, int64_t *payload_bytes, int64_t *
  *      status                int32 [1]     0, or bit 0 set if an id outside [-1, E) was seen
  * Enqueues one kernel on `stream` when S*K <= 4096 and C <= 1024 (decode-sized tables: every
  * workgroup rereads the table and writes its own share of the outputs), otherwise three kernels
- * (count per channel, scan along channels, assign). Both give identical outputs; setting the
- * environment variable MOE_LAYOUT_SMALL=0 forces the three-kernel form (read on every call).
- * No output may alias an input or another output. */
+ * (count per channel, scan along channels, assign). Both forms give identical outputs; the choice
+ * depends on the sizes only. No output may alias an input or another output. */
 int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
                uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
                int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
                int32_t *slot_idx, int32_t *status, hipStream_t stream);
+
+/* Which form of the layout a call of moe_layout_ex / moe_layout_dispatch_ex takes. The forms give
+ * identical outputs; the choice exists so that tests and benchmarks can run each form on the same
+ * table. */
+typedef enum {
+    MOE_LAYOUT_AUTO = 0,   /* what moe_layout does: one launch when S*K <= 4096 and C <= 1024     */
+    MOE_LAYOUT_MULTI = 1,  /* always the multi-launch form (count, scan, assign)                  */
+    MOE_LAYOUT_SINGLE = 2  /* always the single-launch form; MOE_ERR_UNSUPPORTED where S*K > 4096
+                              or C > 1024                                                        */
+} moe_layout_path;
+
+/* moe_layout with an explicit form: same arguments, outputs and errors, plus `path` (a
+ * moe_layout_path; any other value is MOE_ERR_ARG). */
+int moe_layout_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                  uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                  int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                  int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                  int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t path,
+                  hipStream_t stream);
 
 /* Dispatch pack: for every (t, k) with slot s = slot_idx[t, k] >= 0, write slot s of the window
  * (byte offset s * moe_slot_bytes(H)) as the slot layout above: the bf16 row x[t], or its
@@ -148,12 +167,12 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
  * 六项分别保存什么") and the InputToShare copy of "HCCL Window 模式 (Non-SHMEM) 代码深度剖析"
  * (section 3.6) without a launch between them.
  *
- * When S*K <= 4096 and C <= 1024 (and MOE_LAYOUT_SMALL is not 0) it enqueues ONE kernel: its
- * layout workgroups write the layout outputs while its pack workgroups derive the slots of their
- * own tokens from topk_idx (the number of valid entries before (t, k) in expert-major, token, k
- * order) and store the rows; nothing in it reads slot_idx. Otherwise it enqueues the moe_layout
- * kernels followed by the moe_dispatch kernel. Argument checks, alignment rules and error codes
- * are the union of the two calls'; the window must not overlap any other argument. */
+ * When S*K <= 4096 and C <= 1024 it enqueues ONE kernel: its layout workgroups write the layout
+ * outputs while its pack workgroups derive the slots of their own tokens from topk_idx (the number
+ * of valid entries before (t, k) in expert-major, token, k order) and store the rows; nothing in it
+ * reads slot_idx. Otherwise it enqueues the moe_layout kernels followed by the moe_dispatch
+ * kernel. Argument checks, alignment rules and error codes are the union of the two calls'; the
+ * window must not overlap any other argument. */
 int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                         int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                         int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
@@ -161,6 +180,16 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
                         int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                         const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
                         int64_t window_bytes, hipStream_t stream);
+
+/* moe_layout_dispatch with an explicit form (a moe_layout_path): MOE_LAYOUT_SINGLE is the one
+ * kernel above, MOE_LAYOUT_MULTI the moe_layout kernels followed by the pack. */
+int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                           int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                           int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                           int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                           int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                           const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                           int64_t window_bytes, int32_t path, hipStream_t stream);
 
 /* Combine: y[t] = bf16( sum over k = 0..K-1 ascending with slot_idx[t, k] valid of
  *                       fp32(topk_weights[t, k] * fp32(expert_out row slot_idx[t, k])) ),
@@ -203,17 +232,19 @@ int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert
  *                     staging_bytes must cover S*K rows. Rows that receive nothing keep their
  *                     contents.
  * moe_combine_staged
- * In:  staging as written by moe_combine_scatter; slot_idx int32 [S, K] (only its sign is used:
- *      entries < 0 are skipped, all others read staging row t*K + k); topk_weights fp32 [S, K].
+ * In:  staging as written by moe_combine_scatter, staging_bytes long (MOE_ERR_WINDOW unless it
+ *      covers S*K rows of staging_stride_bytes: (S*K - 1) * stride + 2H bytes); slot_idx int32
+ *      [S, K] (only its sign is used: entries < 0 are skipped, all others read staging row
+ *      t*K + k); topk_weights fp32 [S, K].
  * Out: y bf16 [S, H], fully overwritten. */
 int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                         const int32_t *expand_idx, const int32_t *num_rows, int32_t S, int32_t K,
                         int32_t H, void *staging, int64_t staging_stride_bytes,
                         int64_t staging_bytes, hipStream_t stream);
 
-int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, const int32_t *slot_idx,
-                       const float *topk_weights, int32_t S, int32_t H, int32_t K, void *y,
-                       hipStream_t stream);
+int moe_combine_staged(const void *staging, int64_t staging_stride_bytes, int64_t staging_bytes,
+                       const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
+                       int32_t K, void *y, hipStream_t stream);
 
 /* Unpack: window slots -> compact expert input rows ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析",
  * section 3.9 ShareToOutput, which copies each received slot's token data to the next row of

@@ -2,7 +2,8 @@
 // address and undefined-behaviour sanitizers against the stand-in launchers of abi_stubs.cpp:
 // the size arithmetic at the largest accepted sizes and at hostile int64 arguments, a rejected
 // call for every entry point, and which launchers a valid call reaches (for example that
-// moe_layout_dispatch takes the one-kernel path only for small tables). Pointers are fake device
+// moe_layout_dispatch takes the one-kernel path only for small tables, and each moe_layout_path
+// value reaches its launcher). Pointers are fake device
 // addresses that nothing dereferences. Prints "abi_asan ok" and returns 0 when every check holds.
 #include <cstdint>
 #include <cstdio>
@@ -66,7 +67,25 @@ int main() {
            "scatter row extent beyond int64");
     expect(moe_combine_scatter(A, 14336, 512, I, I, 64, 8, 7168, A, 14336, -5, nullptr) == MOE_ERR_WINDOW,
            "scatter negative staging bytes");
-    expect(moe_combine_staged(A, 100, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_ARG, "staged short stride");
+    expect(moe_combine_staged(A, 100, big, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_ARG, "staged short stride");
+    expect(moe_combine_staged(A, big - 15, big, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_WINDOW,
+           "staged huge staging stride");
+    expect(moe_combine_staged(A, 14336, -5, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_WINDOW,
+           "staged negative staging bytes");
+    expect(moe_layout_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, 3, nullptr) == MOE_ERR_ARG,
+           "layout_ex unknown path");
+    expect(moe_layout_ex(I, 513, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_SINGLE, nullptr) ==
+               MOE_ERR_UNSUPPORTED,
+           "layout_ex single launch at S*K = 4104");
+    expect(moe_layout_ex(I, 2048, 2, 16, 4, 1025, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_SINGLE, nullptr) ==
+               MOE_ERR_UNSUPPORTED,
+           "layout_ex single launch with C above 1024");
+    expect(moe_layout_dispatch_ex(I, 513, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A,
+                                  moe_window_bytes(513, 8, 7168), MOE_LAYOUT_SINGLE, nullptr) == MOE_ERR_UNSUPPORTED,
+           "layout_dispatch_ex single launch at S*K = 4104");
+    expect(moe_layout_dispatch_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A,
+                                  moe_window_bytes(64, 8, 7168), -1, nullptr) == MOE_ERR_ARG,
+           "layout_dispatch_ex negative path");
     expect(moe_unpack(A, big, I, 64, 8, 7168, 1, A, nullptr, I, nullptr) == MOE_ERR_ARG, "unpack fp8 without scales");
     expect(moe_unpack_padded(A, big, I, 256, 64, 8, 7168, 0, 16, big, A, nullptr, I, I, I, nullptr) == MOE_ERR_ARG,
            "unpack_padded out_rows beyond the limit");
@@ -81,8 +100,33 @@ int main() {
     const int64_t win = moe_window_bytes(512, 8, 7168);
     stubs::reset();
     expect(moe_layout(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, nullptr) == MOE_OK &&
+               only(stubs::kLayoutSmall, 1),
+           "layout at S*K = 512 -> the single launch");
+    stubs::reset();
+    expect(moe_layout(I, 513, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, nullptr) == MOE_OK &&
                only(stubs::kLayout, 1),
-           "layout -> launch_layout");
+           "layout at S*K = 4104 -> the multi-launch form");
+    stubs::reset();
+    expect(moe_layout(I, 2048, 2, 16, 4, 1025, U, I, I, I, I, I, I, I, I, nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1),
+           "layout with C above 1024 -> the multi-launch form");
+    stubs::reset();
+    expect(moe_layout_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_AUTO, nullptr) == MOE_OK &&
+               only(stubs::kLayoutSmall, 1),
+           "layout_ex auto at S*K = 512 -> the single launch");
+    stubs::reset();
+    expect(moe_layout_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_MULTI, nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1),
+           "layout_ex multi at S*K = 512 -> the multi-launch form");
+    stubs::reset();
+    expect(moe_layout_ex(I, 512, 8, 256, 8, 128, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_SINGLE, nullptr) ==
+                   MOE_OK &&
+               only(stubs::kLayoutSmall, 1),
+           "layout_ex single at S*K = 4096 -> the single launch");
+    stubs::reset();
+    expect(moe_layout_ex(I, 513, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_AUTO, nullptr) == MOE_OK &&
+               only(stubs::kLayout, 1),
+           "layout_ex auto at S*K = 4104 -> the multi-launch form");
     stubs::reset();
     expect(moe_layout_dispatch(I, 512, 8, 256, 8, 128, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win,
                                nullptr) == MOE_OK &&
@@ -103,13 +147,21 @@ int main() {
                                moe_window_bytes(2048, 2, 16), nullptr) == MOE_OK &&
                only(stubs::kLayout, 1, stubs::kPack, 1),
            "layout_dispatch with C above 1024 -> layout + pack");
-    setenv("MOE_LAYOUT_SMALL", "0", 1);
     stubs::reset();
-    expect(moe_layout_dispatch(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win, nullptr) ==
-                   MOE_OK &&
+    expect(moe_layout_dispatch_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win,
+                                  MOE_LAYOUT_MULTI, nullptr) == MOE_OK &&
                only(stubs::kLayout, 1, stubs::kPack, 1),
-           "MOE_LAYOUT_SMALL=0 -> layout + pack");
-    unsetenv("MOE_LAYOUT_SMALL");
+           "layout_dispatch_ex multi at S*K = 512 -> layout + pack");
+    stubs::reset();
+    expect(moe_layout_dispatch_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 1, 0, A, win,
+                                  MOE_LAYOUT_SINGLE, nullptr) == MOE_OK &&
+               only(stubs::kLayoutDispatchSmall, 1),
+           "layout_dispatch_ex single at S*K = 512 -> one kernel");
+    stubs::reset();
+    expect(moe_layout_dispatch_ex(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 2, 0, A, win,
+                                  MOE_LAYOUT_AUTO, nullptr) == MOE_OK &&
+               only(stubs::kLayoutDispatchSmall, 1),
+           "layout_dispatch_ex auto at S*K = 512 -> one kernel");
     stubs::reset();
     expect(moe_dispatch(A, I, 64, 7168, 8, 1, 3, A, win, nullptr) == MOE_OK && only(stubs::kPack, 1),
            "dispatch -> launch_pack");
@@ -124,9 +176,13 @@ int main() {
                MOE_ERR_WINDOW,
            "combine_scatter one byte short");
     stubs::reset();
-    expect(moe_combine_staged(A, 14336, I, F, 64, 7168, 8, A, nullptr) == MOE_OK &&
+    expect(moe_combine_staged(A, 14336, 511LL * 14336 + 14336, I, F, 64, 7168, 8, A, nullptr) == MOE_OK &&
                only(stubs::kCombineStaged, 1),
-           "combine_staged");
+           "combine_staged with exactly S*K rows of staging");
+    expect(moe_combine_staged(A, 14336, 511LL * 14336 + 14335, I, F, 64, 7168, 8, A, nullptr) == MOE_ERR_WINDOW,
+           "combine_staged one byte short");
+    expect(moe_combine_staged(A, 16384, 511LL * 16384 + 14336, I, F, 64, 7168, 8, A, nullptr) == MOE_OK,
+           "combine_staged: the last row needs only 2H bytes");
     stubs::reset();
     expect(moe_unpack(A, win, I, 64, 8, 7168, 1, A, F, I, nullptr) == MOE_OK && only(stubs::kUnpack, 1),
            "unpack");

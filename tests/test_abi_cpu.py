@@ -265,8 +265,10 @@ def test_combine_scatter_validation(kw, err):
     assert scatter_call(**kw) == err
 
 
-def staged_call(stg=A, sstride=14336, slot=A, w=A, S=64, H=7168, K=8, y=A):
-    return moe._lib.moe_combine_staged(stg, sstride, slot, w, S, H, K, y, None)
+def staged_call(stg=A, sstride=14336, sbytes=None, slot=A, w=A, S=64, H=7168, K=8, y=A):
+    if sbytes is None:
+        sbytes = S * K * sstride
+    return moe._lib.moe_combine_staged(stg, sstride, sbytes, slot, w, S, H, K, y, None)
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -277,9 +279,39 @@ def staged_call(stg=A, sstride=14336, slot=A, w=A, S=64, H=7168, K=8, y=A):
     (dict(y=A + 8), moe.MOE_ERR_ALIGN),
     (dict(w=A + 1), moe.MOE_ERR_ALIGN),
     (dict(S=0), moe.MOE_ERR_ARG),
+    (dict(sbytes=(64 * 8 - 1) * 14336 + 2 * 7168 - 1), moe.MOE_ERR_WINDOW),
+    (dict(sbytes=-1), moe.MOE_ERR_WINDOW),
+    (dict(sstride=2**62, sbytes=2**63 - 1), moe.MOE_ERR_WINDOW),
 ])
 def test_combine_staged_validation(kw, err):
     assert staged_call(**kw) == err
+
+
+def layout_ex_call(path, topk=A, S=64, K=8, E=256, P=8, C=16):
+    return moe._lib.moe_layout_ex(topk, S, K, E, P, C, *([A] * 9), path, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(path=3), moe.MOE_ERR_ARG),
+    (dict(path=-1), moe.MOE_ERR_ARG),
+    (dict(path=moe.MOE_LAYOUT_SINGLE, S=513), moe.MOE_ERR_UNSUPPORTED),
+    (dict(path=moe.MOE_LAYOUT_SINGLE, S=2048, K=2, E=16, P=4, C=1025), moe.MOE_ERR_UNSUPPORTED),
+    (dict(path=moe.MOE_LAYOUT_MULTI, topk=NULL), moe.MOE_ERR_ARG),
+    (dict(path=moe.MOE_LAYOUT_MULTI, E=250), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_layout_ex_validation(kw, err):
+    assert layout_ex_call(**kw) == err
+
+
+def test_layout_dispatch_ex_validation():
+    nb = 513 * 8 * 14848
+    lib = moe._lib
+    assert lib.moe_layout_dispatch_ex(A, 513, 8, 256, 8, 16, *([A] * 9), A, 7168, 0, 0, A, nb,
+                                      moe.MOE_LAYOUT_SINGLE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layout_dispatch_ex(A, 64, 8, 256, 8, 16, *([A] * 9), A, 7168, 0, 0, A, nb, 7,
+                                      None) == moe.MOE_ERR_ARG
+    assert lib.moe_layout_dispatch_ex(A, 64, 8, 256, 8, 16, *([A] * 9), A, 7168, 0, 0, A, 0,
+                                      moe.MOE_LAYOUT_MULTI, None) == moe.MOE_ERR_WINDOW
 
 
 def test_dedup_window_bytes():

@@ -29,7 +29,6 @@ def test_abi_layer_under_sanitizers(tmp_path):
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
-    env.pop("MOE_LAYOUT_SMALL", None)
     run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "abi_asan ok" in run.stdout

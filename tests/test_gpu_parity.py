@@ -68,9 +68,9 @@ def poisoned_layout(moe, S, K, E, P, C):
     return out
 
 
-def gpu_layout(moe, idx, E, P, C):
+def gpu_layout(moe, idx, E, P, C, path=None):
     S, K = idx.shape
-    lay = moe.moe_layout(to_dev(idx), E, P, C, out=poisoned_layout(moe, S, K, E, P, C))
+    lay = moe.moe_layout(to_dev(idx), E, P, C, out=poisoned_layout(moe, S, K, E, P, C), path=path)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in lay._asdict().items()}
 
@@ -82,6 +82,18 @@ def assert_layout_equal(got, ref, what=""):
             bad = np.argwhere(g != ref[key])[:5]
             raise AssertionError(f"{what} {key} differs at {bad.tolist()}")
     assert int(got["status"][0]) == ref["status"], what
+
+
+def checked_layout(moe, idx, E, P, C, path=None):
+    """The HIP layout of the host table idx (device tensors, for later HIP calls) and the oracle's
+    layout of the same table, after asserting that the two agree on every output. Expected values
+    downstream are computed from the oracle's layout only."""
+    S, K = idx.shape
+    lay = moe.moe_layout(to_dev(idx), E, P, C, out=poisoned_layout(moe, S, K, E, P, C), path=path)
+    torch.cuda.synchronize()
+    ref = oracle.layout(idx, E, P, C)
+    assert_layout_equal({k: v.cpu().numpy() for k, v in lay._asdict().items()}, ref, "chained layout")
+    return lay, ref
 
 
 def gpu_dispatch(moe, x_bits, slot, quant, src_rank=0):
@@ -122,18 +134,15 @@ def assert_bf16_within_ulp(got, ref, what=""):
 # ---------------------------------------------------------------- layout
 
 
-# Small tables go to the single-launch layout unless MOE_LAYOUT_SMALL=0 (read on every call);
-# the tests run both paths on the same inputs.
-LAYOUT_PATHS = ["auto", "three_launch"]
+# Small tables go to the single-launch layout under MOE_LAYOUT_AUTO; MOE_LAYOUT_MULTI forces the
+# three-launch form. The tests run both on the same inputs through moe_layout_ex /
+# moe_layout_dispatch_ex.
+LAYOUT_PATHS = {"auto": 0, "three_launch": 1}
 
 
-@pytest.fixture(params=LAYOUT_PATHS)
-def layout_path(request, monkeypatch):
-    if request.param == "three_launch":
-        monkeypatch.setenv("MOE_LAYOUT_SMALL", "0")
-    else:
-        monkeypatch.delenv("MOE_LAYOUT_SMALL", raising=False)
-    return request.param
+@pytest.fixture(params=sorted(LAYOUT_PATHS))
+def layout_path(request):
+    return LAYOUT_PATHS[request.param]
 
 
 @pytest.mark.parametrize("cfg", sorted(WORKLOADS))
@@ -142,7 +151,7 @@ def test_layout_workloads(moe, cfg, layout_path):
     idx = inputs(cfg)["topk_idx"]
     for C in sorted({w.C, 1, 3, min(w.S, 4096)}):
         note(f"layout cfg{cfg} {w.describe()} C={C} path={layout_path}")
-        assert_layout_equal(gpu_layout(moe, idx, w.E, w.P, C), oracle.layout(idx, w.E, w.P, C),
+        assert_layout_equal(gpu_layout(moe, idx, w.E, w.P, C, layout_path), oracle.layout(idx, w.E, w.P, C),
                             f"cfg{cfg} C={C}")
 
 
@@ -171,7 +180,7 @@ def test_layout_tiny_adversarial(moe, case, layout_path):
     rng = np.random.default_rng(seed)
     idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
     note(f"layout tiny {case} path={layout_path}")
-    assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), str(case))
+    assert_layout_equal(gpu_layout(moe, idx, E, P, C, layout_path), oracle.layout(idx, E, P, C), str(case))
 
 
 def test_layout_special_tables(moe, layout_path):
@@ -185,24 +194,24 @@ def test_layout_special_tables(moe, layout_path):
     for name, idx in cases.items():
         for C in (1, 3, S):
             note(f"layout special {name} C={C} path={layout_path}")
-            assert_layout_equal(gpu_layout(moe, idx, E, P, C), oracle.layout(idx, E, P, C), name)
+            assert_layout_equal(gpu_layout(moe, idx, E, P, C, layout_path), oracle.layout(idx, E, P, C), name)
 
 
 # ---------------------------------------------------------------- layout + dispatch in one call
 
 
-def gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank=0):
+def gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank=0, path=None):
     S, K = idx.shape
     H = x_bits.shape[1]
     win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
     lay = moe.moe_layout_dispatch(to_dev(idx), E, P, C, bf16_dev(x_bits), win, quant, src_rank,
-                                  out=poisoned_layout(moe, S, K, E, P, C))
+                                  out=poisoned_layout(moe, S, K, E, P, C), path=path)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in lay._asdict().items()}, win.cpu().numpy().reshape(S * K, -1)
 
 
-def check_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank, what):
-    got, win = gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank)
+def check_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank, what, path=None):
+    got, win = gpu_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank, path)
     ref = oracle.layout(idx, E, P, C)
     assert_layout_equal(got, ref, what)
     H = x_bits.shape[1]
@@ -213,12 +222,12 @@ def check_layout_dispatch(moe, idx, x_bits, E, P, C, quant, src_rank, what):
 @pytest.mark.parametrize("cfg,quant", [(1, 0), (1, 1), (2, 0), (2, 1), (2, 2), (3, 0)])
 def test_layout_dispatch_workloads(moe, cfg, quant, layout_path):
     """One call for the layout and the pack: one kernel at workloads 1 and 2, the separate kernels
-    at workload 3 (and everywhere with MOE_LAYOUT_SMALL=0)."""
+    at workload 3 (and everywhere with MOE_LAYOUT_MULTI)."""
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
     note(f"layout_dispatch cfg{cfg} quant {quant} path={layout_path}")
     check_layout_dispatch(moe, inp["topk_idx"], inp["x"], w.E, w.P, w.C, quant, 5,
-                          f"cfg{cfg} quant {quant}")
+                          f"cfg{cfg} quant {quant}", layout_path)
 
 
 FUSED_CASES = [
@@ -251,7 +260,7 @@ def test_layout_dispatch_tiny(moe, case, layout_path):
     x[0, :] = 0.0
     xb = f32_to_bf16_input(x)
     note(f"layout_dispatch tiny {case} path={layout_path}")
-    check_layout_dispatch(moe, idx, xb, E, P, C, quant, seed, str(case))
+    check_layout_dispatch(moe, idx, xb, E, P, C, quant, seed, str(case), layout_path)
 
 
 # ---------------------------------------------------------------- dispatch
@@ -473,8 +482,8 @@ def run_unpack(moe, lay_slot, x_bits, S, K, H, E, quant, n_dev):
 def test_unpack_workloads(moe, cfg, quant):
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
-    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
-    slot = lay.slot_idx.cpu().numpy()
+    lay, ref = checked_layout(moe, inp["topk_idx"], w.E, w.P, w.C)
+    slot = ref["slot_idx"]
     note(f"unpack cfg{cfg} quant {quant}")
     ex, sc, idx = run_unpack(moe, slot, inp["x"], w.S, w.K, w.H, w.E, quant, lay.expert_slot_base[w.E:])
     rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(inp["x"], slot, quant, 7), w.H, quant)
@@ -491,9 +500,9 @@ def test_unpack_partial_and_empty(moe):
     idx_tab = random_tiny_routing(rng, S, K, E, p_mask=0.4)
     xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
     for quant in (0, 1, 2):
-        lay = moe.moe_layout(to_dev(idx_tab), E, P, 3)
-        slot = lay.slot_idx.cpu().numpy()
-        n = int((slot >= 0).sum())
+        lay, ref = checked_layout(moe, idx_tab, E, P, 3)
+        slot = ref["slot_idx"]
+        n = int(ref["expert_slot_base"][E])
         ex, sc, idx = run_unpack(moe, slot, xb, S, K, H, E, quant, lay.expert_slot_base[E:])
         rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(xb, slot, quant, 7), H, quant)
         assert np.array_equal(ex[:n], rex) and np.array_equal(idx[:n], ridx)
@@ -534,9 +543,9 @@ def assert_padded_equal(got, ref, what):
 def test_unpack_padded_workloads(moe, cfg, quant):
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
-    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
-    slot = lay.slot_idx.cpu().numpy()
-    esb = lay.expert_slot_base.cpu().numpy()
+    lay, ref_lay = checked_layout(moe, inp["topk_idx"], w.E, w.P, w.C)
+    slot = ref_lay["slot_idx"]
+    esb = ref_lay["expert_slot_base"]
     regions = oracle.dispatch_slots(inp["x"], slot, quant, 3)
     # (alignment, rows relative to the aligned total): exact fit, extra padding rows, truncation
     cases = [(1, 0), (16, 37), (128, -1000)] if w.S * w.K > 4096 else \
@@ -558,9 +567,9 @@ def test_unpack_padded_tiny_and_degenerate(moe, H):
     tab = random_tiny_routing(rng, S, K, E, p_mask=0.3)
     tab[:, :] = np.where(np.isin(tab, [2, 3]), -1, tab)  # experts 2 and 3 receive nothing
     xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
-    lay = moe.moe_layout(to_dev(tab), E, P, 3)
-    slot = lay.slot_idx.cpu().numpy()
-    esb = lay.expert_slot_base.cpu().numpy()
+    lay, ref_lay = checked_layout(moe, tab, E, P, 3)
+    slot = ref_lay["slot_idx"]
+    esb = ref_lay["expert_slot_base"]
     for quant in (0, 1):
         regions = oracle.dispatch_slots(xb, slot, quant, 3)
         for A, R in ((1, 1), (5, 64), (64, 1000), (7, int(esb[-1])), (3, 17)):
@@ -568,7 +577,7 @@ def test_unpack_padded_tiny_and_degenerate(moe, H):
             got = run_unpack_padded(moe, lay, xb, S, K, H, E, quant, A, R)
             ref = oracle.unpack_padded(regions, esb, H, quant, A, R)
             assert_padded_equal(got, ref, f"tiny quant {quant} A={A} R={R}")
-    empty = moe.moe_layout(to_dev(np.full((S, K), -1, np.int32)), E, P, 3)
+    empty, _ = checked_layout(moe, np.full((S, K), -1, np.int32), E, P, 3)
     got = run_unpack_padded(moe, empty, xb, S, K, H, E, 0, 8, 20)
     assert np.all(got[2] == -1) and not got[0].any() and np.all(got[3] == 0) and got[4][0] == 0
 
@@ -576,9 +585,9 @@ def test_unpack_padded_tiny_and_degenerate(moe, H):
 # ---------------------------------------------------------------- per-rank deduplicated dispatch
 
 
-def gpu_rank_rows(moe, idx, E, P, C):
+def gpu_rank_rows(moe, idx, E, P, C, path=None):
     t = to_dev(idx)
-    lay = moe.moe_layout(t, E, P, C)
+    lay, _ = checked_layout(moe, idx, E, P, C, path)
     S, K = idx.shape
     out = moe.RankRows(torch.full((S, K), -7, dtype=torch.int32, device=DEV),
                        torch.full((P + 1,), -7, dtype=torch.int32, device=DEV))
@@ -594,7 +603,7 @@ def test_rank_rows_workloads(moe, cfg, layout_path):
     ref_rr, ref_base = oracle.rank_rows(idx, w.E, w.P)
     for C in sorted({w.C, 1, 3}):
         note(f"rank_rows cfg{cfg} C={C} path={layout_path}")
-        _, out = gpu_rank_rows(moe, idx, w.E, w.P, C)
+        _, out = gpu_rank_rows(moe, idx, w.E, w.P, C, layout_path)
         assert np.array_equal(out.rank_row_idx.cpu().numpy(), ref_rr), C
         assert np.array_equal(out.rank_token_base.cpu().numpy(), ref_base), C
 
@@ -621,14 +630,15 @@ def dedup_dispatch(moe, x_bits, idx, E, P, C, H, quant=0):
     return lay, rr, win
 
 
-def check_expansion(moe, win, rr, lay, x_bits, E, P, H, quant, prefill=None):
-    """Expand the dedup rows and compare with the oracle's unpack of the K-fold window."""
+def check_expansion(moe, win, rr, lay, ref_slot, x_bits, E, P, H, quant, prefill=None):
+    """Expand the dedup rows and compare with the oracle's unpack of the K-fold window built from
+    the oracle's slots ref_slot (lay is the HIP layout of the same table, already checked)."""
     S, K = lay.slot_idx.shape
     out = prefill
     got = moe.moe_expand_dedup(win, rr.rank_row_idx, lay.slot_idx, lay.expert_slot_base[E:], P, H, quant,
                                out=out)
     torch.cuda.synchronize()
-    rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(x_bits, lay.slot_idx.cpu().numpy(), quant, 5), H, quant)
+    rex, ridx, rsc = oracle.unpack(oracle.dispatch_slots(x_bits, ref_slot, quant, 5), H, quant)
     n = rex.shape[0]
     ex = got.expand_x.view(torch.uint8).cpu().numpy().reshape(S * K, -1)
     assert np.array_equal(ex[:n], rex)
@@ -652,7 +662,8 @@ def test_dispatch_dedup_workloads(moe, cfg, quant):
     assert np.array_equal(rows[:m, : geo.tail_end], ref)
     assert np.all(rows[m:] == POISON)  # rows past M untouched
     # expansion to expert-major rows equals the K-fold unpack
-    check_expansion(moe, win, rr, lay, inp["x"], w.E, w.P, w.H, quant)
+    ref_slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    check_expansion(moe, win, rr, lay, ref_slot, inp["x"], w.E, w.P, w.H, quant)
 
 
 def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
@@ -674,7 +685,8 @@ def test_dedup_tiny_masks_duplicates_and_bad_ids(moe):
             pre = moe.Unpacked(torch.full((S * K, width), 0xCD, dtype=torch.uint8, device=DEV),
                                torch.full((S * K,), -2.0, dtype=torch.float32, device=DEV) if quant else None,
                                torch.full((S * K, 3), -3, dtype=torch.int32, device=DEV))
-            got, n = check_expansion(moe, win, rr, lay, x, E, P, H, quant, prefill=pre)
+            ref_slot = oracle.layout(tab, E, P, C)["slot_idx"]
+            got, n = check_expansion(moe, win, rr, lay, ref_slot, x, E, P, H, quant, prefill=pre)
             assert np.all(got.expand_idx.cpu().numpy()[n:] == -3)  # rows past N keep their contents
             assert np.all(got.expand_x.cpu().numpy()[n:] == 0xCD)
 
@@ -697,7 +709,7 @@ def test_dedup_at_maximum_tokens_and_ranks(moe, S, K, E, P, C):
     geo = oracle.slot_geometry(H, 1)
     rows = win.view(-1, geo.slot_bytes).cpu().numpy()
     assert np.array_equal(rows[: ref.shape[0], : geo.tail_end], ref)
-    check_expansion(moe, win, rr, lay, x, E, P, H, 1)
+    check_expansion(moe, win, rr, lay, oracle.layout(tab, E, P, C)["slot_idx"], x, E, P, H, 1)
 
 
 def test_unpack_padded_at_its_limits(moe):
@@ -710,12 +722,12 @@ def test_unpack_padded_at_its_limits(moe):
         idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
         idx[: E // K + 1] = np.arange(2 * (E // K + 1), dtype=np.int32).reshape(-1, 2) % E  # every expert used
         x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
-        lay = moe.moe_layout(to_dev(idx), E, P, 3)
-        esb = lay.expert_slot_base.cpu().numpy()
+        lay, ref_lay = checked_layout(moe, idx, E, P, 3)
+        esb = ref_lay["expert_slot_base"]
         assert np.all(np.diff(esb) > 0)
         note(f"unpack_padded limits E={E} A={A} R={R}")
         got = run_unpack_padded(moe, lay, x, S, K, H, E, 1, A, R)
-        regions = oracle.dispatch_slots(x, lay.slot_idx.cpu().numpy(), 1, 3)
+        regions = oracle.dispatch_slots(x, ref_lay["slot_idx"], 1, 3)
         ref = oracle.unpack_padded(regions, esb, H, 1, A, R)
         assert int(ref[4]) == (1 if E * A > R else 0)
         assert_padded_equal(got, ref, f"limits E={E}")
@@ -795,12 +807,14 @@ def test_two_pass_combine_workloads(moe, cfg):
     against the oracle's two passes (and so against the gather combine)."""
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
-    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
-    slot = lay.slot_idx.cpu().numpy()
-    n = int(lay.expert_slot_base[w.E].item())
+    lay, ref_lay = checked_layout(moe, inp["topk_idx"], w.E, w.P, w.C)
+    slot = ref_lay["slot_idx"]
+    n = int(ref_lay["expert_slot_base"][w.E])
     win = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=DEV)
     moe.moe_dispatch(bf16_dev(inp["x"]), lay.slot_idx, win, 0, 0)
     un = moe.moe_unpack(win, lay.expert_slot_base[w.E:], w.S, w.K, w.H, 0)
+    # the triples the scatter is given must be the oracle's (checked before they are used)
+    _, ref_idx, _ = oracle.unpack(oracle.dispatch_slots(inp["x"], slot, 0, 0), w.H, 0)
     eo = expert_out(cfg)
     wts = to_dev(inp["topk_weights"])
     stride = -(-2 * w.H // 512) * 512  # the page's 512-byte rows
@@ -810,8 +824,8 @@ def test_two_pass_combine_workloads(moe, cfg):
                             w.K, staging=staging, staging_stride_bytes=stride)
     y = moe.moe_combine_staged(staging, lay.slot_idx, wts, w.H, staging_stride_bytes=stride)
     torch.cuda.synchronize()
-    idx = un.expand_idx.cpu().numpy()
-    ref_stg = oracle.combine_scatter(eo, idx, n, w.S, w.K)
+    assert np.array_equal(un.expand_idx.cpu().numpy()[:n], ref_idx)
+    ref_stg = oracle.combine_scatter(eo, ref_idx, n, w.S, w.K)
     got_stg = staging.view(w.S * w.K, stride).cpu().numpy()[:, : 2 * w.H].view(np.uint16)
     live = (slot >= 0).reshape(-1)
     assert np.array_equal(got_stg[live], ref_stg[live])
@@ -826,8 +840,8 @@ def test_two_pass_combine_masked_and_partial(moe):
     rng = np.random.default_rng(44)
     S, K, E, P, H = 70, 6, 10, 5, 272
     tab = random_tiny_routing(rng, S, K, E, p_mask=0.35)
-    lay = moe.moe_layout(to_dev(tab), E, P, 4)
-    slot = lay.slot_idx.cpu().numpy()
+    lay, ref_lay = checked_layout(moe, tab, E, P, 4)
+    slot = ref_lay["slot_idx"]
     n = int((slot >= 0).sum())
     rows = f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))
     wts = rng.random((S, K)).astype(np.float32)
@@ -881,7 +895,7 @@ def test_combine_from_window_round_trip(moe):
     w = WORKLOADS[3]
     inp = inputs(3)
     x = bf16_dev(inp["x"])
-    lay = moe.moe_layout(to_dev(inp["topk_idx"]), w.E, w.P, w.C)
+    lay, ref_lay = checked_layout(moe, inp["topk_idx"], w.E, w.P, w.C)
     win = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=DEV)
     moe.moe_dispatch(x, lay.slot_idx, win, 0)
     wts = to_dev(inp["topk_weights"])
@@ -889,8 +903,11 @@ def test_combine_from_window_round_trip(moe):
                         expert_rows=w.S * w.K, hidden=w.H)
     torch.cuda.synchronize()
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
-    slot = lay.slot_idx.cpu().numpy()
-    rows = win.cpu().numpy().reshape(w.S * w.K, -1)[:, : 2 * w.H].copy().view(np.uint16)
+    slot = ref_lay["slot_idx"]
+    regions = oracle.dispatch_slots(inp["x"], slot, 0, 0)
+    n = regions.shape[0]
+    assert np.array_equal(win.cpu().numpy().reshape(w.S * w.K, -1)[:n, : regions.shape[1]], regions)
+    rows = np.ascontiguousarray(regions[:, : 2 * w.H]).view(np.uint16)
     assert np.array_equal(got, oracle.combine(rows, slot, inp["topk_weights"]))
     xr = oracle.bf16_bits_to_f32(inp["x"]).astype(np.float64)
     assert np.all(np.abs(oracle.bf16_bits_to_f32(got) - xr) <= np.abs(xr) * 2.0**-7)
