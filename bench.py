@@ -7,10 +7,16 @@ whole-step throughput in GB/s of algorithmic bytes, tokens/s, per-kernel event
 timings, the roofline of the dominant kernel and the CPU oracle timed on the
 host cores as a reported baseline.
 
+The dispatch is moe_dispatch_ws (the planned pack with its workspace: a plan
+kernel, then the pack kernel; the token-order moe_dispatch is timed beside it in
+extras.dispatch_token_order).
+
 Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
 at distinct addresses, so each step reads its inputs from HBM rather than from
 the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); extras.warm_same_buffers repeats the timing with
-one set of buffers. extras.copy_ceiling_GB/s is a 1 GiB device-to-device copy.
+one set of buffers. ceilings holds the library's own 1 GiB probes (write-only
+fill, read-only stream, copy); each kernel also reports its bandwidth against
+the ceiling of its own read/write mix, (r + w) / (r / read + w / fill).
 extras.fused_layout_dispatch times the same eager steps with the layout and the pack
 in one moe_layout_dispatch call (one kernel for decode-sized tables).
 extras.graph_replay times the same step captured in HIP graphs (one per input
@@ -22,13 +28,15 @@ puts 16 steps in one graph so that the replay's own launch cost is shared.
 
 Timing: value and ms_per_step come from the K timed steps with nothing recorded
 between the kernels (wall clock between two device synchronisations). The same
-K steps then run again with an event before and after every kernel; kernels
-holds those event statistics per call (layout, dispatch = the pack, combine) and
-for the sums layout+dispatch and layout+dispatch+combine, each with its bytes,
-GB/s, fraction of 8 TB/s, tokens/s and fraction of the measured copy ceiling.
+K steps then run again with an event before and after every call; kernels
+holds those event statistics per call (layout, dispatch = plan + pack, combine)
+and for the sums layout+dispatch and layout+dispatch+combine, each with its
+bytes, GB/s, fraction of 8 TB/s, tokens/s and fraction of its pattern ceiling.
 Each event adds a few microseconds to the interval it bounds, so the event
 figures are upper bounds on the kernel durations; ms_per_step_with_events is the
-step time of that second pass.
+step time of that second pass; roofline.achieved uses its figure for the
+dominant call. kernels_isolated then times each call alone, K launches back to
+back over the same rotated inputs with one event at each end.
 
 Algorithmic bytes (what the method must move; zero padding and the window
 reservation are not traffic):
@@ -147,24 +155,49 @@ def cpu_model():
     return "cpu model unknown"
 
 
-def copy_ceiling(torch, dev, mib=1024, iters=10):
-    """Device-to-device copy of 1 GiB with torch (read + write bytes per second): the practical
-    bandwidth ceiling next to the 8 TB/s specification."""
+def ceilings(torch, moe, dev, mib=1024, iters=10):
+    """The library's bandwidth probes over 1 GiB buffers (write-only fill, read-only stream, copy
+    of read + write bytes), GB/s: the practical ceilings of the three access patterns next to the
+    8 TB/s specification."""
     n = mib * 2**20
     src = torch.empty(n, dtype=torch.uint8, device=dev)
-    src.fill_(1)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    gbs = 2 * n * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    moe.moe_probe_fill(src)
+    out = {}
+    for name, fn, nbytes in (("fill", lambda: moe.moe_probe_fill(dst), n),
+                             ("read", lambda: moe.moe_probe_read(src, sink), n),
+                             ("copy", lambda: moe.moe_probe_copy(src, dst), 2 * n)):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del src, dst
-    return gbs
+    return out
+
+
+def rw_split(w, C, n_valid):
+    """(read, write) algorithmic bytes of each call, for the pattern ceilings."""
+    S, H, K, E, P = w.S, w.H, w.K, w.E, w.P
+    payload = 2 * H if w.quant == 0 else H
+    return {
+        "layout": (4 * S * K, S * P + 4 * (P + E) + 4 * (P + 1 + E + 1) + 4 * S * K + 4 * (P + E) * C),
+        "dispatch": (2 * S * H + 4 * S * K, n_valid * (payload + 12 + (4 if w.quant else 0))),
+        "combine": (8 * S * K + n_valid * 2 * H, 2 * S * H),
+    }
+
+
+def pattern_ceiling(ceil, r, wbytes):
+    """Bandwidth ceiling of a call that reads r and writes wbytes bytes, if reads and writes share
+    the memory one after the other at the probes' read and fill rates."""
+    if not ceil:
+        return None
+    return (r + wbytes) / (r / ceil["read"] + wbytes / ceil["fill"])
 
 
 def time_fused_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
@@ -187,7 +220,8 @@ def time_fused_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
-def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1):
+def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1,
+                      ws=None):
     """The same step captured in HIP graphs and replayed: the device time of a step without the
     Python launch overhead, which dominates at decode sizes. per_graph = 1: one graph per input set,
     one step per replay; per_graph > 1: that many steps (cycling over the input sets) in one graph,
@@ -198,7 +232,7 @@ def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
             moe.moe_layout_dispatch(topk, w.E, w.P, C, x, window, w.quant, 0, out=lay)
         else:
             moe.moe_layout(topk, w.E, w.P, C, out=lay)
-            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
     graphs = []
@@ -329,6 +363,39 @@ def time_dedup(moe, torch, w, C, lay, window, inputs, n_valid, kfold_pack_bytes,
     return out
 
 
+def time_fp8_workload_pack(args, torch, moe, dev, window, stream):
+    """The fp8 DynamicQuant pack on its own workload (S=4096, H=7168, E=256, P=8, K=8, x ~ 2*N(0,1)
+    with 1% outliers x50): moe_dispatch_ws in fp8 mode, K launches back to back over --rotate copies
+    of x (cold), one event at each end; its algorithmic bytes and fraction of 8 TB/s."""
+    from workloads import WORKLOADS, make_inputs
+
+    w4 = WORKLOADS[4]
+    inp = make_inputs(w4, with_expert_out=False)
+    n_valid = int(((inp["topk_idx"] >= 0) & (inp["topk_idx"] < w4.E)).sum())
+    x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [x0] + [x0.clone() for _ in range(1, max(1, args.rotate))]
+    lay4 = moe.moe_layout(torch.from_numpy(inp["topk_idx"]).to(dev), w4.E, w4.P, w4.C)
+    nws = moe.moe_dispatch_workspace_bytes(w4.S, w4.K, w4.quant)
+    ws4 = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    for i in range(3):
+        moe.moe_dispatch_ws(xs[i % len(xs)], lay4.slot_idx, window, ws4, w4.quant, 0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        moe.moe_dispatch_ws(xs[i % len(xs)], lay4.slot_idx, window, ws4, w4.quant, 0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    nb = algorithmic_bytes(w4, w4.C, n_valid)["dispatch"]
+    gbs = nb / (avg_us * 1e-6) / 1e9
+    del xs, x0
+    return {"workload": w4.describe(), "avg_us": round(avg_us, 2), "bytes": nb, "GB/s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "input_sets": max(1, args.rotate),
+            "timing": "K launches back to back, events at both ends"}
+
+
 def time_unpack(moe, torch, w, lay, window, n_valid, stream, iters=20):
     """moe_unpack of the last dispatched window (outside the timed step): the grouped-GEMM input."""
     payload = 2 * w.H if w.quant == 0 else w.H
@@ -405,6 +472,8 @@ def main():
     sets = [base] + [tuple(t.clone() for t in base) for _ in range(1, max(1, args.rotate))]
     lay = moe.empty_layout(w.S, w.K, w.E, w.P, C, dev)
     window = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=dev)
+    nws = moe.moe_dispatch_workspace_bytes(w.S, w.K, w.quant)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -420,7 +489,7 @@ def main():
     def step(i, sets_used):
         x, topk, wts, eo = sets_used[i % len(sets_used)]
         moe.moe_layout(topk, w.E, w.P, C, out=lay)
-        moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+        moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
     def timed(sets_used):
@@ -445,7 +514,7 @@ def main():
             e[0].record(stream)
             moe.moe_layout(topk, w.E, w.P, C, out=lay)
             e[1].record(stream)
-            moe.moe_dispatch(x, lay.slot_idx, window, w.quant, 0)
+            moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
             e[2].record(stream)
             moe.moe_combine(eo, lay.slot_idx, wts, y=y)
             e[3].record(stream)
@@ -471,24 +540,75 @@ def main():
                 "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                 "tokens_per_s": round(w.S / (avg_us * 1e-6), 1),
             }
-            if copy_gbs:
-                kernels[k]["frac_copy_ceiling"] = round(gbs / copy_gbs, 4)
+            pc = pattern_ceilings.get(k)
+            if pc:
+                kernels[k]["frac_pattern_ceiling"] = round(gbs / pc, 4)
         return kernels, 1e3 * elapsed / args.steps, 1e3 * elapsed_events / args.steps
 
+    def isolated(sets_used, calls):
+        """Each call alone, K launches back to back cycling over sets_used, one event at each end:
+        the average duration of one launch (with the short gaps between queued launches)."""
+        out = {}
+        for name, fn in calls.items():
+            for i in range(3):
+                fn(sets_used[i % len(sets_used)])
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                fn(sets_used[i % len(sets_used)])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            avg_us = 1e3 * e0.elapsed_time(e1) / args.steps
+            gbs = nbytes[name] / (avg_us * 1e-6) / 1e9 if name in nbytes else None
+            out[name] = {"avg_us": round(avg_us, 2)}
+            if gbs is not None:
+                out[name].update({"bytes": nbytes[name], "GB/s": round(gbs, 1),
+                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                pc = pattern_ceilings.get(name)
+                if pc:
+                    out[name]["frac_pattern_ceiling"] = round(gbs / pc, 4)
+        return out
+
+    calls = {
+        "layout": lambda st: moe.moe_layout(st[1], w.E, w.P, C, out=lay),
+        "dispatch": lambda st: moe.moe_dispatch_ws(st[0], lay.slot_idx, window, ws, w.quant, 0),
+        "combine": lambda st: moe.moe_combine(st[3], lay.slot_idx, st[2], y=y),
+    }
+
     nbytes = algorithmic_bytes(w, C, n_valid)
-    copy_gbs = None if args.no_extras else copy_ceiling(torch, dev)
+    ceil = None if args.no_extras else ceilings(torch, moe, dev)
+    split = rw_split(w, C, n_valid)
+    pattern_ceilings = {}
+    if ceil:
+        for k, (r, wb) in split.items():
+            pattern_ceilings[k] = pattern_ceiling(ceil, r, wb)
+        for k, parts in (("layout+dispatch", ("layout", "dispatch")),
+                         ("layout+dispatch+combine", ("layout", "dispatch", "combine"))):
+            r = sum(split[p][0] for p in parts)
+            wb = sum(split[p][1] for p in parts)
+            pattern_ceilings[k] = pattern_ceiling(ceil, r, wb)
     kernels, ms_per_step, ms_per_step_events = timed(sets)
+    kernels_isolated = isolated(sets, calls)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
-    kernel_key = {"dispatch": {0: "pack_bf16", 1: "pack_fp8", 2: "pack_int8"}[w.quant],
+    planned = moe.moe_dispatch_workspace_bytes(w.S, w.K, w.quant) > 0
+    kernel_key = {"dispatch": {0: "pack_bf16_planned" if planned else "pack_bf16", 1: "pack_fp8",
+                               2: "pack_int8"}[w.quant],
                   "combine": "combine"}[dom]
     traffic = traffic_from_profiles(f"{kernel_key}:{w.name}")
     roofline = {
         "bound": "hbm", "kernel": kernel_key,
+        "launches": ("plan + pack kernels of one moe_dispatch_ws call" if dom == "dispatch" and planned
+                     else "one kernel"),
         "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(kernels[dom]["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
         "algorithmic_bytes_per_launch": nbytes[dom],
+        "avg_launch_us": kernels[dom]["avg_us"],
+        "timing": "events before and after the call in each of the K timed steps (the kernels' stream)",
+        "isolated_avg_launch_us": kernels_isolated[dom]["avg_us"],
     }
     out = {
         "metric": METRIC,
@@ -511,11 +631,18 @@ def main():
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_with_events": round(ms_per_step_events, 4),
         "kernels": kernels,
+        "kernels_isolated": kernels_isolated,
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if ceil:
+        out["ceilings"] = dict(ceil, unit="GB/s", method="library probes (include/moe_probe.h) over 1 GiB; "
+                               "copy counts read + write bytes", pattern_ceiling_GB_s={
+                                   k: round(v, 1) for k, v in pattern_ceilings.items()})
     if not args.no_extras:
-        out["extras"] = {"copy_ceiling_GB/s": round(copy_gbs, 1), "copy_method": "torch copy_ (hipMemcpyAsync device to device) of 1 GiB, read+write bytes"}
+        out["extras"] = {}
+        tok = isolated(sets, {"dispatch": lambda st: moe.moe_dispatch(st[0], lay.slot_idx, window, w.quant, 0)})
+        out["extras"]["dispatch_token_order"] = tok["dispatch"]
         if len(sets) > 1:
             warm, warm_ms, _ = timed(sets[:1])
             out["extras"]["warm_same_buffers"] = {
@@ -524,16 +651,18 @@ def main():
         out["extras"]["fused_layout_dispatch"] = time_fused_eager(args, torch, moe, w, C, sets, lay, window,
                                                                   y, total_bytes)
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
-                                                          total_bytes)
+                                                          total_bytes, ws=ws)
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
         fused["one_kernel_layout_dispatch"] = w.S * w.K <= 4096 and C <= 1024
         out["extras"]["graph_replay_fused_layout_dispatch"] = fused
         if w.S * w.K <= 4096:  # decode sizes: 16 steps per graph, the replay's own cost shared
             out["extras"]["graph_replay_16_steps_per_graph"] = {
                 "separate": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
-                                              per_graph=16),
+                                              per_graph=16, ws=ws),
                 "fused_layout_dispatch": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                            total_bytes, fused=True, per_graph=16)}
+        if w.name == "dsv3_prefill":
+            out["extras"]["fp8_dynquant_pack"] = time_fp8_workload_pack(args, torch, moe, dev, window, stream)
         out["extras"]["unpack"] = time_unpack(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["unpack_padded"] = time_unpack_padded(moe, torch, w, lay, window, n_valid, stream)
         out["extras"]["two_pass_combine"] = time_two_pass_combine(moe, torch, w, lay, window, sets[0],

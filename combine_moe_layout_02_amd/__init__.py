@@ -34,10 +34,14 @@ MOE_LAYOUT_SINGLE = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_layout_ex", "moe_dispatch",
+    "moe_dispatch_workspace_bytes", "moe_dispatch_ws",
     "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
     "moe_unpack", "moe_unpack_padded", "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup",
     "moe_expand_dedup", "moe_status_string",
 )
+
+# include/moe_probe.h: bandwidth probes for the measurement, not part of the path
+PROBES = ("moe_probe_fill", "moe_probe_read", "moe_probe_copy")
 
 
 def _load():
@@ -47,7 +51,7 @@ def _load():
             "(hipcc, gfx950). There is no fallback implementation."
         )
     lib = ctypes.CDLL(_LIB_PATH)
-    missing = [name for name in EXPORTED if not hasattr(lib, name)]
+    missing = [name for name in EXPORTED + PROBES if not hasattr(lib, name)]
     if missing:
         raise ImportError(f"{_LIB_PATH} is stale (missing {missing}); rebuild it with "
                           "`python combine_moe_layout_02_amd/build.py`")
@@ -59,6 +63,8 @@ def _load():
         "moe_layout": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [P]),
         "moe_layout_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [I32, P]),
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
+        "moe_dispatch_workspace_bytes": (I64, [I32, I32, I32]),
+        "moe_dispatch_ws": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P, I64, P]),
         "moe_layout_dispatch": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
                                 [P, I32, I32, I32, P, I64, P]),
         "moe_layout_dispatch_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
@@ -74,6 +80,9 @@ def _load():
         "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
                                              P, P, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_probe_fill": (ctypes.c_int, [P, I64, P]),
+        "moe_probe_read": (ctypes.c_int, [P, I64, P, P]),
+        "moe_probe_copy": (ctypes.c_int, [P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -224,6 +233,35 @@ def moe_dispatch(x, slot_idx, window, quant=MOE_QUANT_NONE, src_rank=0, stream=N
     return window
 
 
+def moe_dispatch_workspace_bytes(S, K, quant=MOE_QUANT_NONE):
+    v = _lib.moe_dispatch_workspace_bytes(int(S), int(K), int(quant))
+    if v < 0:
+        _check(int(v))
+    return int(v)
+
+
+def moe_dispatch_ws(x, slot_idx, window, workspace, quant=MOE_QUANT_NONE, src_rank=0, stream=None):
+    """moe_dispatch with a caller workspace (a device buffer of at least
+    moe_dispatch_workspace_bytes(S, K, quant) bytes, or None when that size is 0): the same window
+    bytes, written by the planned pack where it applies."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 2, x.device)
+    _need(window, "window", device=x.device)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _need(workspace, "workspace", device=x.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_dispatch_ws(_ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank), _ptr(window),
+                                nbytes, ws_ptr, ws_bytes, _stream(x.device, stream)))
+    return window
+
+
 def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, window,
                         quant=MOE_QUANT_NONE, src_rank=0, out=None, stream=None, path=None):
     """moe_layout and moe_dispatch in one call (one kernel for small tables); returns the Layout.
@@ -334,6 +372,30 @@ def moe_combine_staged(staging, slot_idx, topk_weights, hidden, staging_stride_b
                                    _ptr(slot_idx), _ptr(topk_weights), S, H, K, _ptr(y),
                                    _stream(dev, stream)))
     return y
+
+
+def moe_probe_fill(dst, stream=None):
+    """Write-only bandwidth probe over the whole device tensor dst (measurement only)."""
+    _need(dst, "dst")
+    _check(_lib.moe_probe_fill(_ptr(dst), dst.numel() * dst.element_size(), _stream(dst.device, stream)))
+
+
+def moe_probe_read(src, sink, stream=None):
+    """Read-only bandwidth probe over the whole device tensor src; sink is a device int32 [1]."""
+    _need(src, "src")
+    _need(sink, "sink", torch.int32, device=src.device)
+    _check(_lib.moe_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                               _stream(src.device, stream)))
+
+
+def moe_probe_copy(src, dst, stream=None):
+    """Copy probe: dst = src, both device tensors of the same byte size."""
+    _need(src, "src")
+    _need(dst, "dst", device=src.device)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must have the same byte size")
+    _check(_lib.moe_probe_copy(_ptr(src), _ptr(dst), n, _stream(src.device, stream)))
 
 
 def moe_dedup_window_bytes(S, K, P, H):
@@ -525,7 +587,7 @@ __all__ = [
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MOE_LAYOUT_AUTO",
     "MOE_LAYOUT_MULTI", "MOE_LAYOUT_SINGLE", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 ]

@@ -161,6 +161,34 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
 }
 
+int64_t moe_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t quant) {
+    const int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    return moe::pack_planned_used(S, K, quant) ? moe::pack_plan_bytes(S, K) : 0;
+}
+
+int moe_dispatch_ws(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                    int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
+                    void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (!x || !slot_idx || !window) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    const bool planned = moe::pack_planned_used(S, K, quant);
+    if (planned && !workspace) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
+    if (planned && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    if (planned && workspace_bytes < moe::pack_plan_bytes(S, K)) return MOE_ERR_WINDOW;
+    if (planned)
+        return from_hip(moe::launch_pack_planned(x, slot_idx, S, H, K, src_rank, window, workspace,
+                                                 stream));
+    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+}
+
 int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
                            int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
                            int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
@@ -384,7 +412,7 @@ const char *moe_status_string(int status) {
         case MOE_OK: return "ok";
         case MOE_ERR_ARG: return "invalid argument (null pointer or size out of range)";
         case MOE_ERR_ALIGN: return "misaligned pointer or stride";
-        case MOE_ERR_WINDOW: return "buffer too small: the window (S*K*moe_slot_bytes(H) bytes) or staging rows";
+        case MOE_ERR_WINDOW: return "buffer too small: the window (S*K*moe_slot_bytes(H) bytes), staging rows or workspace";
         case MOE_ERR_UNSUPPORTED: return "unsupported shape (E % P != 0, H % 16 != 0 or S too large)";
         case MOE_ERR_HIP: return "HIP launch error";
         default: return "unknown status";

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "moe.h"
+#include "moe_probe.h"
 
 namespace moe {
 
@@ -84,6 +85,50 @@ hipError_t launch_expand_dedup(const void *window, const int32_t *rank_row_idx,
 
 hipError_t launch_pack(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                        int32_t quant, int32_t src_rank, void *window, hipStream_t stream);
+
+// The planned bf16 pack (pack_planned.hip) runs for tables of at least this many entries; smaller
+// tables and the quantised modes take the token-order pack of launch_pack.
+constexpr int64_t kPlannedMinEntries = 8192;
+
+// Shape of the planned pack's work: token chunks of Tc = 2^lt tokens (the largest power of two with
+// Tc * K <= 1024), chunk c owned by XCD c % 8, each XCD's list holding nsx chunks of Tc * K
+// records; slots are bucketed by slot >> shift (at most 1024 buckets).
+struct PlanShape {
+    int lt;
+    int nsub;
+    int nsx;
+    int shift;
+};
+
+inline PlanShape plan_shape(int32_t S, int32_t K) {
+    PlanShape p;
+    int lk = 0;
+    while ((1 << lk) < K) ++lk;
+    p.lt = 10 - lk;
+    const int Tc = 1 << p.lt;
+    p.nsub = (S + Tc - 1) / Tc;
+    p.nsx = (p.nsub + 7) / 8;
+    int bits = 0;
+    while ((int64_t(1) << bits) < (int64_t)S * K) ++bits;
+    p.shift = bits > 10 ? bits - 10 : 0;
+    return p;
+}
+
+// True when moe_dispatch_ws takes the planned pack for (S, K, quant).
+inline bool pack_planned_used(int32_t S, int32_t K, int32_t quant) {
+    return quant == MOE_QUANT_NONE && (int64_t)S * K >= kPlannedMinEntries;
+}
+
+// Workspace bytes of the planned pack's record lists (8 bytes per record) for (S, K).
+inline int64_t pack_plan_bytes(int32_t S, int32_t K) {
+    const PlanShape p = plan_shape(S, K);
+    return (int64_t)8 * p.nsx * ((int64_t)K << p.lt) * 8;
+}
+
+// Plan kernel + planned pack kernel; workspace holds pack_plan_bytes(S, K) bytes, 16-byte aligned.
+hipError_t launch_pack_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H,
+                               int32_t K, int32_t src_rank, void *window, void *workspace,
+                               hipStream_t stream);
 
 hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,

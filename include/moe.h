@@ -160,6 +160,32 @@ int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, i
                  int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                  hipStream_t stream);
 
+/* Dispatch pack with a caller workspace: the same window bytes as moe_dispatch (same arguments,
+ * same meaning, same bytes written and left untouched), written in an order that HBM absorbs
+ * faster. The CAM pack ("HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6 InputToShare) writes
+ * each token's copies as soon as its row is read, which spreads the writes in flight over every
+ * expert's slot range; here a plan kernel first lists each chunk of tokens' (slot, token, k)
+ * records by slot, and the pack kernel then writes every chunk in slot order from rows its XCD
+ * has just read.
+ *
+ * moe_dispatch_workspace_bytes(S, K, quant): bytes the workspace needs (0 when the call takes the
+ *      token-order pack: quantised modes, and bf16 tables of fewer than 8192 entries); a negative
+ *      moe_status on bad S, K or quant.
+ * moe_dispatch_ws: as moe_dispatch, plus
+ *      workspace       device buffer, 16-byte aligned, of workspace_bytes >=
+ *                      moe_dispatch_workspace_bytes(S, K, quant) (MOE_ERR_WINDOW otherwise; it may
+ *                      be NULL when that size is 0, MOE_ERR_ARG if it is NULL otherwise). Its
+ *                      contents are overwritten; the caller owns it and must not use it for
+ *                      anything else until the call's kernels have finished. Calls that may run at
+ *                      the same time need workspaces of their own.
+ * Enqueues the plan kernel and the pack kernel (or only the token-order pack when the workspace
+ * size is 0) on `stream`. */
+int64_t moe_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t quant);
+
+int moe_dispatch_ws(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                    int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
+                    void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* Layout and dispatch pack in one call: the outputs of moe_layout (same arguments, same meaning)
  * and the window of moe_dispatch (same x, H, quant, src_rank, window, window_bytes), bit for bit.
  * It is the fused single-kernel layout + pack for decode-sized batches, where both steps are

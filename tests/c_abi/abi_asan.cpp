@@ -94,6 +94,21 @@ int main() {
            "dedup small window");
     expect(moe_expand_dedup(A, big, I, I, I, 64, 8, 0, 7168, 0, A, nullptr, I, nullptr) == MOE_ERR_ARG,
            "expand P = 0");
+    {
+        const int64_t wsb = moe_dispatch_workspace_bytes(4096, 8, 0);
+        const int64_t wbig = moe_window_bytes(4096, 8, 7168);
+        expect(wsb == 8LL * 4 * 128 * 8 * 8, "dispatch workspace bytes at S=4096, K=8");
+        expect(moe_dispatch_workspace_bytes(MOE_MAX_TOKENS, MOE_MAX_K, 0) == 8LL * 128 * 64 * 16 * 8,
+               "dispatch workspace bytes at the largest sizes");
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 0, 0, A, wbig, nullptr, wsb, nullptr) == MOE_ERR_ARG,
+               "dispatch_ws without a workspace");
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 0, 0, A, wbig, A, wsb - 1, nullptr) == MOE_ERR_WINDOW,
+               "dispatch_ws one workspace byte short");
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 0, 0, A, wbig, base + 8, wsb, nullptr) == MOE_ERR_ALIGN,
+               "dispatch_ws misaligned workspace");
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 0, 0, A, wbig, A, -big, nullptr) == MOE_ERR_WINDOW,
+               "dispatch_ws negative workspace bytes");
+    }
     expect(only(stubs::kLaunchers, 0), "no launcher reached by a rejected call");
 
     // valid calls and the launchers they reach
@@ -165,6 +180,28 @@ int main() {
     stubs::reset();
     expect(moe_dispatch(A, I, 64, 7168, 8, 1, 3, A, win, nullptr) == MOE_OK && only(stubs::kPack, 1),
            "dispatch -> launch_pack");
+    {
+        const int64_t wbig = moe_window_bytes(4096, 8, 7168);
+        const int64_t wsb = moe_dispatch_workspace_bytes(4096, 8, 0);
+        stubs::reset();
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 0, 0, A, wbig, A, wsb, nullptr) == MOE_OK &&
+                   only(stubs::kPackPlanned, 1),
+               "dispatch_ws bf16 at S*K = 32768 -> planned pack");
+        stubs::reset();
+        expect(moe_dispatch_ws(A, I, 1024, 7168, 8, 0, 0, A, moe_window_bytes(1024, 8, 7168), A,
+                               moe_dispatch_workspace_bytes(1024, 8, 0), nullptr) == MOE_OK &&
+                   only(stubs::kPackPlanned, 1),
+               "dispatch_ws bf16 at S*K = 8192 -> planned pack");
+        stubs::reset();
+        expect(moe_dispatch_ws(A, I, 1023, 7168, 8, 0, 0, A, moe_window_bytes(1023, 8, 7168), nullptr, 0,
+                               nullptr) == MOE_OK &&
+                   only(stubs::kPack, 1),
+               "dispatch_ws bf16 at S*K = 8184 -> token-order pack, no workspace needed");
+        stubs::reset();
+        expect(moe_dispatch_ws(A, I, 4096, 7168, 8, 1, 0, A, wbig, nullptr, 0, nullptr) == MOE_OK &&
+                   only(stubs::kPack, 1),
+               "dispatch_ws fp8 -> token-order quantised pack, no workspace needed");
+    }
     stubs::reset();
     expect(moe_combine(A, 14848, 512, I, F, 64, 7168, 8, A, nullptr) == MOE_OK && only(stubs::kCombine, 1),
            "combine -> launch_combine");

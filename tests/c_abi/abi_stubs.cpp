@@ -53,6 +53,11 @@ hipError_t launch_pack(const void *, const int32_t *, int32_t, int32_t, int32_t,
     ++calls[stubs::kPack];
     return hipSuccess;
 }
+hipError_t launch_pack_planned(const void *, const int32_t *, int32_t, int32_t, int32_t, int32_t, void *, void *,
+                               hipStream_t) {
+    ++calls[stubs::kPackPlanned];
+    return hipSuccess;
+}
 hipError_t launch_combine(const void *, int64_t, int64_t, const int32_t *, const float *, int32_t, int32_t,
                           int32_t, void *, hipStream_t) {
     ++calls[stubs::kCombine];

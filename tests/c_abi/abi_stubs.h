@@ -5,7 +5,7 @@
 
 namespace stubs {
 enum Launcher {
-    kLayout, kLayoutSmall, kLayoutDispatchSmall, kRankRows, kPackDedup, kExpandDedup, kPack, kCombine,
+    kLayout, kLayoutSmall, kLayoutDispatchSmall, kRankRows, kPackDedup, kExpandDedup, kPack, kPackPlanned, kCombine,
     kCombineScatter, kCombineStaged, kUnpackPadded, kUnpack, kLaunchers
 };
 extern int calls[kLaunchers];

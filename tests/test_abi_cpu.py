@@ -12,12 +12,13 @@ import combine_moe_layout_02_amd as moe
 from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "moe.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")
 A = 0x10000  # a fake, 512-byte aligned device address; never dereferenced on these paths
 NULL = None
 
 
-def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
+def declared_functions(header=HEADER):
+    text = open(header, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
 
@@ -28,8 +29,25 @@ def test_header_declares_the_boundary():
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(moe._LIB_PATH)
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(PROBE_HEADER):
         assert hasattr(lib, name), name
+
+
+def test_probe_header_declares_the_probes():
+    assert declared_functions(PROBE_HEADER) == sorted(moe.PROBES)
+
+
+@pytest.mark.parametrize("fn,args", [
+    ("moe_probe_fill", (NULL, 1 << 20, None)),
+    ("moe_probe_fill", (A, 1000, None)),          # not a multiple of 16
+    ("moe_probe_fill", (A + 8, 1 << 20, None)),   # misaligned
+    ("moe_probe_read", (A, 0, A, None)),
+    ("moe_probe_read", (A, 1 << 20, NULL, None)),
+    ("moe_probe_copy", (A, NULL, 1 << 20, None)),
+    ("moe_probe_copy", (A, A, -16, None)),
+])
+def test_probe_validation(fn, args):
+    assert getattr(moe._lib, fn)(*args) == moe.MOE_ERR_ARG
 
 
 def test_slot_geometry_matches_golden():
@@ -112,6 +130,44 @@ def dispatch_call(x=A, slot=A, S=64, H=7168, K=8, quant=0, window=A, nbytes=None
 ])
 def test_dispatch_validation(kw, err):
     assert dispatch_call(**kw) == err
+
+
+def dispatch_ws_call(x=A, slot=A, S=4096, H=7168, K=8, quant=0, window=A, nbytes=None, ws=A, wsbytes=None):
+    if nbytes is None:
+        nbytes = S * K * 14848
+    if wsbytes is None:
+        wsbytes = max(0, moe._lib.moe_dispatch_workspace_bytes(S, K, quant))
+    return moe._lib.moe_dispatch_ws(x, slot, S, H, K, quant, 0, window, nbytes, ws, wsbytes, None)
+
+
+def test_dispatch_workspace_bytes():
+    # chunks of Tc = 2^floor(log2(1024 / K')) tokens (K' = K rounded up to a power of two), ceil(S / Tc)
+    # chunks over 8 XCD lists of ceil(chunks / 8) chunks, Tc * K records of 8 bytes each
+    assert moe.moe_dispatch_workspace_bytes(4096, 8) == 8 * 4 * 128 * 8 * 8
+    assert moe.moe_dispatch_workspace_bytes(8192, 8) == 8 * 8 * 128 * 8 * 8
+    assert moe.moe_dispatch_workspace_bytes(1024, 8) == 8 * 1 * 1024 * 8
+    assert moe.moe_dispatch_workspace_bytes(4096, 3) == 8 * 2 * 256 * 3 * 8
+    assert moe.moe_dispatch_workspace_bytes(65536, 16) == 8 * 128 * 64 * 16 * 8
+    assert moe.moe_dispatch_workspace_bytes(1023, 8) == 0  # S*K below 8192: token-order pack
+    assert moe.moe_dispatch_workspace_bytes(4096, 8, moe.MOE_QUANT_FP8_E4M3_DYN) == 0
+    assert moe.moe_dispatch_workspace_bytes(4096, 8, moe.MOE_QUANT_INT8_DYN) == 0
+    assert moe._lib.moe_dispatch_workspace_bytes(0, 8, 0) == moe.MOE_ERR_ARG
+    assert moe._lib.moe_dispatch_workspace_bytes(16, 8, 3) == moe.MOE_ERR_ARG
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(x=NULL), moe.MOE_ERR_ARG),
+    (dict(ws=NULL), moe.MOE_ERR_ARG),
+    (dict(ws=A + 8), moe.MOE_ERR_ALIGN),
+    (dict(wsbytes=8 * 4 * 128 * 8 * 8 - 1), moe.MOE_ERR_WINDOW),
+    (dict(nbytes=4096 * 8 * 14848 - 1), moe.MOE_ERR_WINDOW),
+    (dict(window=A + 256), moe.MOE_ERR_ALIGN),
+    (dict(quant=3), moe.MOE_ERR_ARG),
+    (dict(H=7160), moe.MOE_ERR_UNSUPPORTED),
+    (dict(K=17), moe.MOE_ERR_ARG),
+])
+def test_dispatch_ws_validation(kw, err):
+    assert dispatch_ws_call(**kw) == err
 
 
 def layout_dispatch_call(topk=A, S=64, K=8, E=256, P=8, C=16, outs=None, x=A, H=7168, quant=0,

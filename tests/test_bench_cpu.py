@@ -66,3 +66,22 @@ def test_cpu_baseline_fields():
     assert set(cb["stage_ms"]) == {"layout", "dispatch", "combine"}
     assert all(v >= 0 for v in cb["stage_ms"].values())
     assert cb["sample"].startswith("1 full steps")
+
+
+@pytest.mark.parametrize("cfg", sorted(EXPECTED))
+def test_read_write_split_adds_up(cfg):
+    """The read/write split behind the pattern ceilings covers exactly the algorithmic bytes."""
+    w = WORKLOADS[cfg]
+    nb = bench.algorithmic_bytes(w, w.C, w.S * w.K)
+    split = bench.rw_split(w, w.C, w.S * w.K)
+    for k in ("layout", "dispatch", "combine"):
+        assert sum(split[k]) == nb[k], k
+
+
+def test_pattern_ceiling():
+    ceil = {"read": 7000.0, "fill": 6000.0}
+    assert bench.pattern_ceiling(ceil, 1, 0) == pytest.approx(7000.0)
+    assert bench.pattern_ceiling(ceil, 0, 1) == pytest.approx(6000.0)
+    # equal bytes each way: the harmonic mean of the two rates
+    assert bench.pattern_ceiling(ceil, 5, 5) == pytest.approx(2 / (1 / 7000 + 1 / 6000))
+    assert bench.pattern_ceiling(None, 1, 1) is None

@@ -453,6 +453,87 @@ def test_dispatch_bf16_copies_non_finite_bits(moe):
     assert_window_equal(win, oracle.dispatch_slots(xb, slot, 0, 1), oracle.slot_geometry(H, 0), "non-finite bf16")
 
 
+# ---------------------------------------------------------------- dispatch with a workspace (planned pack)
+
+
+def gpu_dispatch_ws(moe, x_bits, slot, quant, src_rank=0, ws_poison=0x5C):
+    S, H = x_bits.shape
+    K = slot.shape[1]
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    nws = moe.moe_dispatch_workspace_bytes(S, K, quant)
+    ws = torch.full((max(nws, 16),), ws_poison, dtype=torch.uint8, device=DEV) if nws else None
+    moe.moe_dispatch_ws(bf16_dev(x_bits), to_dev(slot), win, ws, quant, src_rank)
+    torch.cuda.synchronize()
+    return win.cpu().numpy().reshape(S * K, -1)
+
+
+@pytest.mark.parametrize("cfg,quant", [(1, 0), (2, 0), (3, 0), (4, 1), (4, 0), (5, 0), (3, 2)])
+def test_dispatch_ws_workloads(moe, cfg, quant):
+    """moe_dispatch_ws on the workloads: the planned pack at workloads 3-5 in bf16, the token-order
+    pack elsewhere; window bytes equal to the oracle's, nothing else written."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    slot = oracle.layout(inp["topk_idx"], w.E, w.P, w.C)["slot_idx"]
+    note(f"dispatch_ws cfg{cfg} quant {quant}")
+    win = gpu_dispatch_ws(moe, inp["x"], slot, quant, src_rank=2)
+    assert_window_equal(win, oracle.dispatch_slots(inp["x"], slot, quant, 2), oracle.slot_geometry(w.H, quant),
+                        f"ws cfg{cfg} quant {quant}")
+
+
+PLANNED_DISPATCH = [
+    # (S, K, H, E, P, p_mask, p_bad_slot, seed): bf16 tables of 8192+ entries take the planned pack
+    (1024, 8, 7168, 256, 8, 0.0, 0.0, 101),    # S*K = 8192: the smallest planned table
+    (1023, 8, 1024, 64, 8, 0.0, 0.0, 102),     # S*K = 8184: token order
+    (8192, 1, 2048, 16, 4, 0.1, 0.0, 103),     # K = 1: chunks of 1024 tokens
+    (3001, 3, 4112, 48, 4, 0.1, 0.02, 104),    # K = 3 (chunks of 256 tokens), ragged last chunk and part
+    (600, 16, 7168, 128, 16, 0.2, 0.0, 105),   # K at its maximum: chunks of 64 tokens
+    (2049, 8, 16384, 256, 8, 0.0, 0.0, 106),   # MOE_MAX_HIDDEN: 16 parts per row
+    (1700, 5, 16, 40, 8, 0.3, 0.05, 107),      # smallest H: one part, mostly tail
+    (9000, 8, 64, 256, 8, 1.0, 0.0, 108),      # everything masked: nothing written
+]
+
+
+@pytest.mark.parametrize("case", PLANNED_DISPATCH)
+def test_dispatch_ws_planned_shapes(moe, case):
+    """Planned-pack chunking at the edges: K in {1, 3, 5, 8, 16}, ragged chunks, masked entries and
+    entries at or past S*K in the slot table, H from 16 to 16384."""
+    S, K, H, E, P, p_mask, p_bad, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask)
+    slot = oracle.layout(idx, E, P, min(S, 128))["slot_idx"]
+    far = (slot < 0) & (rng.random((S, K)) < p_bad * 10)
+    slot = slot.copy()
+    slot[far] = S * K + rng.integers(0, 1000, int(far.sum())).astype(np.int32)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    note(f"dispatch_ws planned {case}")
+    win = gpu_dispatch_ws(moe, xb, slot, 0, src_rank=seed)
+    ref = oracle.dispatch_slots(xb, np.where(slot < S * K, slot, -1), 0, seed)
+    assert_window_equal(win, ref, oracle.slot_geometry(H, 0), str(case))
+
+
+def test_dispatch_ws_any_slot_table_and_reused_workspace(moe):
+    """A random permutation of the slots (not a layout's order) through the planned pack, twice with
+    the same workspace, the second time after the workspace was overwritten: identical windows."""
+    rng = np.random.default_rng(109)
+    S, K, H = 2048, 8, 4096
+    slot = np.full((S, K), -1, np.int32)
+    keep = rng.random((S, K)) < 0.9
+    n = int(keep.sum())
+    slot[keep] = rng.permutation(n).astype(np.int32)
+    x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    ws = torch.full((moe.moe_dispatch_workspace_bytes(S, K),), 0x11, dtype=torch.uint8, device=DEV)
+    ref = oracle.dispatch_slots(x, slot, 0, 4)
+    geo = oracle.slot_geometry(H, 0)
+    xd, sd = bf16_dev(x), to_dev(slot)
+    for rep in range(2):
+        win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+        moe.moe_dispatch_ws(xd, sd, win, ws, 0, 4)
+        torch.cuda.synchronize()
+        note(f"dispatch_ws permuted slots, rep {rep}")
+        assert_window_equal(win.cpu().numpy().reshape(S * K, -1), ref, geo, f"permuted rep {rep}")
+        ws.fill_(0xEE)
+
+
 def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
@@ -941,12 +1022,12 @@ def test_combine_row_stride_and_expert_rows(moe):
 # ---------------------------------------------------------------- determinism
 
 
-@pytest.mark.parametrize("cfg,quant,fused", [(3, 0, False), (2, 0, False), (2, 0, True), (2, 1, True),
-                                             (1, 2, True)])
+@pytest.mark.parametrize("cfg,quant,fused", [(3, 0, False), (3, 0, "ws"), (2, 0, False), (2, 0, True),
+                                             (2, 1, True), (1, 2, True)])
 def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
     """Each kernel twice on identical inputs, outputs poisoned differently before each run: the
-    three-launch layout (workload 3), the single-launch layout (workload 2) and the one-kernel
-    layout + pack (moe_layout_dispatch)."""
+    three-launch layout (workload 3), the planned pack (workload 3, its workspace poisoned too), the
+    single-launch layout (workload 2) and the one-kernel layout + pack (moe_layout_dispatch)."""
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
     idx = to_dev(inp["topk_idx"])
@@ -960,7 +1041,12 @@ def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
         for t in lay:
             t.view(torch.uint8).fill_(poison)
         win = torch.full((moe.moe_window_bytes(w.S, w.K, w.H),), poison, dtype=torch.uint8, device=DEV)
-        if fused:
+        if fused == "ws":
+            moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
+            ws = torch.full((moe.moe_dispatch_workspace_bytes(w.S, w.K, quant),), poison, dtype=torch.uint8,
+                            device=DEV)
+            moe.moe_dispatch_ws(x, lay.slot_idx, win, ws, quant)
+        elif fused:
             moe.moe_layout_dispatch(idx, w.E, w.P, w.C, x, win, quant, out=lay)
         else:
             moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
