@@ -23,6 +23,8 @@ MOE_ERR_ALIGN = -2
 MOE_ERR_WINDOW = -3
 MOE_ERR_UNSUPPORTED = -4
 MOE_ERR_HIP = -5
+MOE_ERR_SCRATCH = -6
+MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 MOE_QUANT_NONE = 0
 MOE_QUANT_FP8_E4M3_DYN = 1
@@ -34,7 +36,7 @@ MOE_LAYOUT_SINGLE = 2
 
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_layout_ex", "moe_dispatch",
-    "moe_dispatch_workspace_bytes", "moe_dispatch_ws",
+    "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc",
     "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
     "moe_unpack", "moe_unpack_padded", "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup",
     "moe_expand_dedup", "moe_status_string",
@@ -65,6 +67,7 @@ def _load():
         "moe_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_dispatch_workspace_bytes": (I64, [I32, I32, I32]),
         "moe_dispatch_ws": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P, I64, P]),
+        "moe_dispatch_noalloc": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, I64, P]),
         "moe_layout_dispatch": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
                                 [P, I32, I32, I32, P, I64, P]),
         "moe_layout_dispatch_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
@@ -259,6 +262,23 @@ def moe_dispatch_ws(x, slot_idx, window, workspace, quant=MOE_QUANT_NONE, src_ra
     nbytes = window.numel() * window.element_size()
     _check(_lib.moe_dispatch_ws(_ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank), _ptr(window),
                                 nbytes, ws_ptr, ws_bytes, _stream(x.device, stream)))
+    return window
+
+
+def moe_dispatch_noalloc(x, slot_idx, window, quant=MOE_QUANT_NONE, src_rank=0, stream=None):
+    """moe_dispatch_ws with the library's fixed device scratch instead of a workspace (allocates
+    nothing; calls that overlap on one GPU race on that scratch). ValueError with MOE_ERR_SCRATCH
+    when the table needs more than MOE_NOALLOC_SCRATCH_BYTES."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 2, x.device)
+    _need(window, "window", device=x.device)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_dispatch_noalloc(_ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank), _ptr(window),
+                                     nbytes, _stream(x.device, stream)))
     return window
 
 
@@ -587,7 +607,8 @@ __all__ = [
     "MOE_ERR_HIP", "MOE_QUANT_NONE", "MOE_QUANT_FP8_E4M3_DYN", "MOE_QUANT_INT8_DYN", "MOE_LAYOUT_AUTO",
     "MOE_LAYOUT_MULTI", "MOE_LAYOUT_SINGLE", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
-    "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
+    "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc", "MOE_ERR_SCRATCH",
+    "MOE_NOALLOC_SCRATCH_BYTES", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string",
 ]

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["layout.hip", "layout_small.hip", "pack.hip", "pack_planned.hip", "combine.hip", "unpack.hip",
-           "probe.hip", "moe_api.cpp"]
+           "probe.hip", "noalloc.hip", "moe_api.cpp"]
 
 # -ffp-contract=off: combine rounds every product and sum to fp32 on its own (no fused multiply-add).
 # -packed-fp32-ops off: scalar fp32 only; no packed fp32 instructions are generated.

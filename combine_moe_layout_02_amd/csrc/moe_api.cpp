@@ -57,6 +57,19 @@ int check_experts(int32_t E, int32_t P) {
 
 namespace moe {
 
+int check_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                   int32_t quant, const void *window, int64_t window_bytes) {
+    if (!x || !slot_idx || !window) return MOE_ERR_ARG;
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(H);
+    if (st != MOE_OK) return st;
+    if (!valid_quant(quant)) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
+    return MOE_OK;
+}
+
 bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
     (void)E;
     (void)P;
@@ -150,14 +163,8 @@ int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t
 int moe_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                  int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                  hipStream_t stream) {
-    if (!x || !slot_idx || !window) return MOE_ERR_ARG;
-    int st = check_tokens(S, K);
+    const int st = moe::check_dispatch(x, slot_idx, S, H, K, quant, window, window_bytes);
     if (st != MOE_OK) return st;
-    st = check_hidden(H);
-    if (st != MOE_OK) return st;
-    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
-    if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
-    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
     return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
 }
 
@@ -171,17 +178,11 @@ int64_t moe_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t quant) {
 int moe_dispatch_ws(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                     int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                     void *workspace, int64_t workspace_bytes, hipStream_t stream) {
-    if (!x || !slot_idx || !window) return MOE_ERR_ARG;
-    int st = check_tokens(S, K);
+    const int st = moe::check_dispatch(x, slot_idx, S, H, K, quant, window, window_bytes);
     if (st != MOE_OK) return st;
-    st = check_hidden(H);
-    if (st != MOE_OK) return st;
-    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
     const bool planned = moe::pack_planned_used(S, K, quant);
     if (planned && !workspace) return MOE_ERR_ARG;
-    if (!aligned(x, 16) || !aligned(slot_idx, 4) || !aligned(window, 512)) return MOE_ERR_ALIGN;
     if (planned && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
-    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
     if (planned && workspace_bytes < moe::pack_plan_bytes(S, K)) return MOE_ERR_WINDOW;
     if (planned)
         return from_hip(moe::launch_pack_planned(x, slot_idx, S, H, K, src_rank, window, workspace,
@@ -415,6 +416,8 @@ const char *moe_status_string(int status) {
         case MOE_ERR_WINDOW: return "buffer too small: the window (S*K*moe_slot_bytes(H) bytes), staging rows or workspace";
         case MOE_ERR_UNSUPPORTED: return "unsupported shape (E % P != 0, H % 16 != 0 or S too large)";
         case MOE_ERR_HIP: return "HIP launch error";
+        case MOE_ERR_SCRATCH:
+            return "table too large for the fixed scratch of moe_dispatch_noalloc (see MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

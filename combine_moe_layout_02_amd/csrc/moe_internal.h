@@ -40,6 +40,11 @@ inline SlotGeom slot_geom(int32_t H, int32_t quant) {
 constexpr int kSmallLayoutEntries = 4096;   // S * K
 constexpr int kSmallLayoutChannels = 1024;  // C
 
+// The argument checks moe_dispatch, moe_dispatch_ws and moe_dispatch_noalloc share (MOE_OK or a
+// negative moe_status; no HIP call).
+int check_dispatch(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                   int32_t quant, const void *window, int64_t window_bytes);
+
 // True when the single-launch layout can take (S, K, E, P, C).
 bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C);
 

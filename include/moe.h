@@ -36,7 +36,8 @@ typedef enum {
     MOE_ERR_WINDOW = -3,      /* window_bytes < moe_window_bytes(S, K, H), or a staging buffer
                                  shorter than its S*K rows                                    */
     MOE_ERR_UNSUPPORTED = -4, /* E % P != 0, H % 16 != 0, or S above MOE_MAX_TOKENS           */
-    MOE_ERR_HIP = -5          /* the HIP runtime reported an error for a launch               */
+    MOE_ERR_HIP = -5,         /* the HIP runtime reported an error for a launch               */
+    MOE_ERR_SCRATCH = -6      /* moe_dispatch_noalloc: the table needs more than its fixed scratch */
 } moe_status;
 
 typedef enum {
@@ -185,6 +186,25 @@ int64_t moe_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t quant);
 int moe_dispatch_ws(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                     int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                     void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* moe_dispatch_ws for callers that cannot allocate (code under HIP graph capture, serving loops
+ * that may not call hipMalloc, harnesses that forbid allocation): the same window bytes and the
+ * same kernels, with the planned pack's record lists in a fixed scratch array that the library
+ * holds in device memory (MOE_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends) instead
+ * of a caller workspace. It allocates nothing.
+ *
+ * Arguments, checks and errors as moe_dispatch, plus MOE_ERR_SCRATCH (nothing enqueued) when
+ * moe_dispatch_workspace_bytes(S, K, quant) exceeds MOE_NOALLOC_SCRATCH_BYTES (bf16 tables up to
+ * 16384 tokens at K = 8 fit). The first call on a device looks up that device's copy of the array;
+ * a failure there is MOE_ERR_HIP. Every call on a GPU uses that GPU's one array: calls that may run
+ * at the same time on one GPU (two streams, two host threads) race on it and must not overlap.
+ * The plan kernel rewrites every record the pack kernel reads, so no call depends on what an
+ * earlier call left in the array. */
+#define MOE_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+int moe_dispatch_noalloc(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                         int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
+                         hipStream_t stream);
 
 /* Layout and dispatch pack in one call: the outputs of moe_layout (same arguments, same meaning)
  * and the window of moe_dispatch (same x, H, quant, src_rank, window, window_bytes), bit for bit.

@@ -170,6 +170,22 @@ def test_dispatch_ws_validation(kw, err):
     assert dispatch_ws_call(**kw) == err
 
 
+def test_noalloc_rejects_tables_beyond_its_scratch():
+    """Checked before any HIP call: the bf16 table whose plan needs more than the fixed scratch, and
+    the ordinary argument errors."""
+    lib = moe._lib
+    assert moe.moe_dispatch_workspace_bytes(16384, 8) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_dispatch_workspace_bytes(16385, 8) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    nb = 16385 * 8 * 14848
+    assert lib.moe_dispatch_noalloc(A, A, 16385, 7168, 8, 0, 0, A, nb, None) == moe.MOE_ERR_SCRATCH
+    assert lib.moe_dispatch_noalloc(A, A, 65536, 16, 16, 0, 0, A, 65536 * 16 * 512, None) == moe.MOE_ERR_SCRATCH
+    assert lib.moe_dispatch_noalloc(NULL, A, 64, 7168, 8, 0, 0, A, nb, None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_noalloc(A, A, 64, 7168, 8, 3, 0, A, nb, None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_noalloc(A, A, 64, 7168, 8, 0, 0, A + 256, nb, None) == moe.MOE_ERR_ALIGN
+    assert lib.moe_dispatch_noalloc(A, A, 4096, 7168, 8, 0, 0, A, 4096 * 8 * 14848 - 1, None) == moe.MOE_ERR_WINDOW
+    assert "scratch" in moe.moe_status_string(moe.MOE_ERR_SCRATCH)
+
+
 def layout_dispatch_call(topk=A, S=64, K=8, E=256, P=8, C=16, outs=None, x=A, H=7168, quant=0,
                          window=A, nbytes=None):
     outs = outs if outs is not None else [A] * 9
