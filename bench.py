@@ -18,7 +18,9 @@ one set of buffers. ceilings holds the library's own 1 GiB probes (write-only
 fill, read-only stream, copy); each kernel also reports its bandwidth against
 the ceiling of its own read/write mix, (r + w) / (r / read + w / fill).
 extras.fused_layout_dispatch times the same eager steps with the layout and the pack
-in one moe_layout_dispatch call (one kernel for decode-sized tables).
+in one moe_layout_dispatch call (one kernel for decode-sized tables), and
+extras.planned_calls_eager the same step through pre-validated calls (moe_plan_*,
+checked once, then one moe_plan_run per launch).
 extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
 bounds the event timings at decode sizes. extras.graph_replay_fused_layout_dispatch
@@ -218,6 +220,33 @@ def time_fused_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
     ms = 1e3 * (time.perf_counter() - t0) / args.steps
     return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
+
+
+def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes, ws):
+    """The step through pre-validated calls (moe_plan_*): one plan per input set made once, then each
+    step runs its plans (moe_plan_run: one short C call per launch, no argument checks), launched
+    eagerly like the timed steps."""
+    plans = []
+    for x, topk, wts, eo in sets:
+        if w.S * w.K <= 4096 and C <= 1024:  # decode sizes: layout + pack in one kernel
+            first = [moe.plan_layout_dispatch(topk, w.E, w.P, C, x, window, lay, w.quant, 0)]
+        else:
+            first = [moe.plan_layout(topk, w.E, w.P, C, lay), moe.plan_dispatch_ws(x, lay.slot_idx, window, ws,
+                                                                                     w.quant, 0)]
+        plans.append([p.run for p in first] + [moe.plan_combine(eo, lay.slot_idx, wts, y).run])
+    n = len(plans)
+    for i in range(args.warmup):
+        for run in plans[i % n]:
+            run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for run in plans[i % n]:
+            run()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1), "launch_calls_per_step": len(plans[0])}
 
 
 def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1,
@@ -650,6 +679,8 @@ def main():
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
         out["extras"]["fused_layout_dispatch"] = time_fused_eager(args, torch, moe, w, C, sets, lay, window,
                                                                   y, total_bytes)
+        out["extras"]["planned_calls_eager"] = time_planned_eager(args, torch, moe, w, C, sets, lay, window, y,
+                                                                  total_bytes, ws)
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                           total_bytes, ws=ws)
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)

@@ -39,7 +39,8 @@ EXPORTED = (
     "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc",
     "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
     "moe_unpack", "moe_unpack_padded", "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup",
-    "moe_expand_dedup", "moe_status_string",
+    "moe_expand_dedup", "moe_status_string", "moe_plan_layout", "moe_plan_dispatch_ws",
+    "moe_plan_layout_dispatch", "moe_plan_combine", "moe_plan_run",
 )
 
 # include/moe_probe.h: bandwidth probes for the measurement, not part of the path
@@ -83,6 +84,12 @@ def _load():
         "moe_unpack_padded": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, I64,
                                              P, P, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_plan_layout": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32] + [P] * 9 + [I32]),
+        "moe_plan_dispatch_ws": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, P, I64, P, I64]),
+        "moe_plan_layout_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32] + [P] * 9 +
+                                     [P, I32, I32, I32, P, I64, I32]),
+        "moe_plan_combine": (ctypes.c_int, [P, P, I64, I64, P, P, I32, I32, I32, P]),
+        "moe_plan_run": (ctypes.c_int, [P, P]),
         "moe_probe_fill": (ctypes.c_int, [P, I64, P]),
         "moe_probe_read": (ctypes.c_int, [P, I64, P, P]),
         "moe_probe_copy": (ctypes.c_int, [P, P, I64, P]),
@@ -418,6 +425,102 @@ def moe_probe_copy(src, dst, stream=None):
     _check(_lib.moe_probe_copy(_ptr(src), _ptr(dst), n, _stream(src.device, stream)))
 
 
+MOE_PLAN_BYTES = 320  # sizeof(moe_plan)
+
+
+class Plan:
+    """A pre-validated call (include/moe.h, moe_plan_*): the arguments were checked once when the
+    plan was made; run() enqueues the call on the current (or given) stream without checking them
+    again. The tensors the plan was made from are kept referenced here, so they stay allocated for
+    the plan's lifetime; they must keep their shapes (do not resize them)."""
+
+    __slots__ = ("_buf", "_addr", "_dev", "_keep", "_run", "_stream_of")
+
+    def __init__(self, dev, keep):
+        self._buf = ctypes.create_string_buffer(MOE_PLAN_BYTES)
+        self._addr = ctypes.addressof(self._buf)
+        self._dev = dev.index if dev.index is not None else torch.cuda.current_device()
+        self._keep = keep
+        self._run = _lib.moe_plan_run
+        self._stream_of = _raw_stream
+
+    def run(self, stream=None):
+        if stream is None and self._stream_of is not None:
+            rc = self._run(self._addr, self._stream_of(self._dev))
+        else:
+            rc = self._run(self._addr, _stream(torch.device("cuda", self._dev), stream))
+        if rc:
+            _check(rc)
+
+
+def plan_layout(topk_idx, num_experts, num_ranks, num_channels, out, path=MOE_LAYOUT_AUTO):
+    """Plan of moe_layout_ex on these buffers (out: a Layout)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    S, K = topk_idx.shape
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    dev = topk_idx.device
+    _need_layout(out, S, K, E, P, C, dev)
+    plan = Plan(dev, (topk_idx, out))
+    _check(_lib.moe_plan_layout(plan._addr, _ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out], int(path)))
+    return plan
+
+
+def plan_dispatch_ws(x, slot_idx, window, workspace, quant=MOE_QUANT_NONE, src_rank=0):
+    """Plan of moe_dispatch_ws on these buffers."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 2, x.device)
+    _need(window, "window", device=x.device)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _need(workspace, "workspace", device=x.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    plan = Plan(x.device, (x, slot_idx, window, workspace))
+    _check(_lib.moe_plan_dispatch_ws(plan._addr, _ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank),
+                                     _ptr(window), window.numel() * window.element_size(), ws_ptr, ws_bytes))
+    return plan
+
+
+def plan_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, window, out, quant=MOE_QUANT_NONE,
+                         src_rank=0, path=MOE_LAYOUT_AUTO):
+    """Plan of moe_layout_dispatch_ex on these buffers (out: a Layout)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    dev = topk_idx.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(window, "window", device=dev)
+    S, K = topk_idx.shape
+    if x.shape[0] != S:
+        raise ValueError("x must have one row per token of topk_idx")
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    _need_layout(out, S, K, E, P, C, dev)
+    plan = Plan(dev, (topk_idx, x, window, out))
+    _check(_lib.moe_plan_layout_dispatch(plan._addr, _ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out],
+                                         _ptr(x), x.shape[1], int(quant), int(src_rank), _ptr(window),
+                                         window.numel() * window.element_size(), int(path)))
+    return plan
+
+
+def plan_combine(expert_out, slot_idx, topk_weights, y):
+    """Plan of moe_combine of a bf16 [R, H] expert_out into y (bf16 [S, H])."""
+    _need(slot_idx, "slot_idx", torch.int32, 2)
+    dev = slot_idx.device
+    _need(expert_out, "expert_out", torch.bfloat16, 2, dev)
+    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
+    _need(y, "y", torch.bfloat16, 2, dev)
+    S, K = slot_idx.shape
+    R, H = expert_out.shape
+    if tuple(topk_weights.shape) != (S, K) or tuple(y.shape) != (S, H):
+        raise ValueError("topk_weights must match slot_idx and y must be [S, H]")
+    plan = Plan(dev, (expert_out, slot_idx, topk_weights, y))
+    _check(_lib.moe_plan_combine(plan._addr, _ptr(expert_out), 2 * H, R, _ptr(slot_idx), _ptr(topk_weights), S, H,
+                                 K, _ptr(y)))
+    return plan
+
+
 def moe_dedup_window_bytes(S, K, P, H):
     v = _lib.moe_dedup_window_bytes(int(S), int(K), int(P), int(H))
     if v < 0:
@@ -610,5 +713,6 @@ __all__ = [
     "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc", "MOE_ERR_SCRATCH",
     "MOE_NOALLOC_SCRATCH_BYTES", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
-    "moe_status_string",
+    "moe_status_string", "Plan", "plan_layout", "plan_dispatch_ws", "plan_layout_dispatch", "plan_combine",
+    "MOE_PLAN_BYTES",
 ]

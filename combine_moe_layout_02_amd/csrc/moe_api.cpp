@@ -7,6 +7,10 @@
 // DeepEP Python entry ("Ascend DeepEP MoE Dispatch Optimization", section "从 Python 接口进入真实调用链").
 
 #include <stdint.h>
+#include <string.h>
+
+#include <cstring>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -78,6 +82,171 @@ bool layout_small_fits(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C) {
 
 }  // namespace moe
 
+namespace {
+
+// Arguments of one call, as validated by its check_* function; run_* launches them unchecked.
+struct LayoutArgs {
+    const int32_t *topk_idx;
+    int32_t S, K, E, P, C;
+    uint8_t *is_token_in_rank;
+    int32_t *num_tokens_per_rank, *num_tokens_per_expert, *rank_prefix_matrix,
+        *expert_prefix_matrix, *rank_slot_base, *expert_slot_base, *slot_idx, *status;
+    int32_t form;  // 1 = single launch, 0 = multi-launch (set by check_layout)
+};
+
+struct DispatchArgs {
+    const void *x;
+    const int32_t *slot_idx;
+    int32_t S, H, K, quant, src_rank;
+    void *window;
+    void *workspace;
+    bool planned;  // set by check_dispatch_ws
+};
+
+struct LayoutDispatchArgs {
+    LayoutArgs layout;
+    const void *x;
+    int32_t H, quant, src_rank;
+    void *window;
+};
+
+struct CombineArgs {
+    const void *expert_out;
+    int64_t row_stride_bytes, expert_rows;
+    const int32_t *slot_idx;
+    const float *topk_weights;
+    int32_t S, H, K;
+    void *y;
+};
+
+// The layout checks shared by moe_layout_ex and moe_layout_dispatch_ex; sets a.form.
+int check_layout(LayoutArgs &a, int32_t path) {
+    if (!a.topk_idx || !a.is_token_in_rank || !a.num_tokens_per_rank || !a.num_tokens_per_expert ||
+        !a.rank_prefix_matrix || !a.expert_prefix_matrix || !a.rank_slot_base ||
+        !a.expert_slot_base || !a.slot_idx || !a.status)
+        return MOE_ERR_ARG;
+    int st = check_tokens(a.S, a.K);
+    if (st != MOE_OK) return st;
+    if (a.E < 1 || a.E > MOE_MAX_EXPERTS || a.P < 1 || a.P > MOE_MAX_RANKS) return MOE_ERR_ARG;
+    if (a.C < 1 || a.C > a.S || a.C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    if (a.E % a.P != 0) return MOE_ERR_UNSUPPORTED;
+    const int form = pick_layout(path, a.S, a.K, a.E, a.P, a.C);
+    if (form < 0) return MOE_ERR_ARG;
+    if (form == 2) return MOE_ERR_UNSUPPORTED;
+    const void *i32[] = {a.topk_idx, a.num_tokens_per_rank, a.num_tokens_per_expert,
+                         a.rank_prefix_matrix, a.expert_prefix_matrix, a.rank_slot_base,
+                         a.expert_slot_base, a.slot_idx, a.status};
+    for (const void *p : i32)
+        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+    a.form = form;
+    return MOE_OK;
+}
+
+int run_layout(const LayoutArgs &a, hipStream_t stream) {
+    if (a.form == 1)
+        return from_hip(moe::launch_layout_small(
+            a.topk_idx, a.S, a.K, a.E, a.P, a.C, a.is_token_in_rank, a.num_tokens_per_rank,
+            a.num_tokens_per_expert, a.rank_prefix_matrix, a.expert_prefix_matrix,
+            a.rank_slot_base, a.expert_slot_base, a.slot_idx, a.status, stream));
+    return from_hip(moe::launch_layout(a.topk_idx, a.S, a.K, a.E, a.P, a.C, a.is_token_in_rank,
+                                       a.num_tokens_per_rank, a.num_tokens_per_expert,
+                                       a.rank_prefix_matrix, a.expert_prefix_matrix,
+                                       a.rank_slot_base, a.expert_slot_base, a.slot_idx, a.status,
+                                       stream));
+}
+
+int check_dispatch_ws(DispatchArgs &a, int64_t window_bytes, int64_t workspace_bytes) {
+    const int st = moe::check_dispatch(a.x, a.slot_idx, a.S, a.H, a.K, a.quant, a.window,
+                                       window_bytes);
+    if (st != MOE_OK) return st;
+    const bool planned = moe::pack_planned_used(a.S, a.K, a.quant);
+    if (planned && !a.workspace) return MOE_ERR_ARG;
+    if (planned && !aligned(a.workspace, 16)) return MOE_ERR_ALIGN;
+    if (planned && workspace_bytes < moe::pack_plan_bytes(a.S, a.K)) return MOE_ERR_WINDOW;
+    a.planned = planned;
+    return MOE_OK;
+}
+
+int run_dispatch_ws(const DispatchArgs &a, hipStream_t stream) {
+    if (a.planned)
+        return from_hip(moe::launch_pack_planned(a.x, a.slot_idx, a.S, a.H, a.K, a.src_rank,
+                                                 a.window, a.workspace, stream));
+    return from_hip(moe::launch_pack(a.x, a.slot_idx, a.S, a.H, a.K, a.quant, a.src_rank,
+                                     a.window, stream));
+}
+
+int check_layout_dispatch(LayoutDispatchArgs &a, int32_t path, int64_t window_bytes) {
+    if (!a.x || !a.window) return MOE_ERR_ARG;
+    int st = check_layout(a.layout, path);
+    if (st != MOE_OK) return st;
+    st = check_hidden(a.H);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(a.quant)) return MOE_ERR_ARG;
+    if (!aligned(a.x, 16) || !aligned(a.window, 512)) return MOE_ERR_ALIGN;
+    if (window_bytes < moe_window_bytes(a.layout.S, a.layout.K, a.H)) return MOE_ERR_WINDOW;
+    return MOE_OK;
+}
+
+int run_layout_dispatch(const LayoutDispatchArgs &a, hipStream_t stream) {
+    const LayoutArgs &l = a.layout;
+    if (l.form == 1)
+        return from_hip(moe::launch_layout_dispatch_small(
+            l.topk_idx, l.S, l.K, l.E, l.P, l.C, l.is_token_in_rank, l.num_tokens_per_rank,
+            l.num_tokens_per_expert, l.rank_prefix_matrix, l.expert_prefix_matrix,
+            l.rank_slot_base, l.expert_slot_base, l.slot_idx, l.status, a.x, a.H, a.quant,
+            a.src_rank, a.window, stream));
+    const int st = run_layout(l, stream);
+    if (st != MOE_OK) return st;
+    return from_hip(moe::launch_pack(a.x, l.slot_idx, l.S, a.H, l.K, a.quant, a.src_rank,
+                                     a.window, stream));
+}
+
+int check_combine(const CombineArgs &a) {
+    if (!a.expert_out || !a.slot_idx || !a.topk_weights || !a.y) return MOE_ERR_ARG;
+    int st = check_tokens(a.S, a.K);
+    if (st != MOE_OK) return st;
+    st = check_hidden(a.H);
+    if (st != MOE_OK) return st;
+    if (a.expert_rows < 0 || a.row_stride_bytes < 2 * (int64_t)a.H) return MOE_ERR_ARG;
+    if (!extent_fits(a.expert_rows, a.row_stride_bytes)) return MOE_ERR_ARG;
+    if (a.row_stride_bytes % 16 != 0 || !aligned(a.expert_out, 16) || !aligned(a.y, 16) ||
+        !aligned(a.slot_idx, 4) || !aligned(a.topk_weights, 4))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+int run_combine(const CombineArgs &a, hipStream_t stream) {
+    return from_hip(moe::launch_combine(a.expert_out, a.row_stride_bytes, a.expert_rows,
+                                        a.slot_idx, a.topk_weights, a.S, a.H, a.K, a.y, stream));
+}
+
+// What a moe_plan holds: a tag, the call kind and its checked arguments.
+struct PlanRecord {
+    static constexpr uint64_t kMagic = 0x6d6f65706c616e31ull;  // "moeplan1"
+    enum Kind : int32_t { kNone = 0, kLayout = 1, kDispatch = 2, kLayoutDispatch = 3, kCombine = 4 };
+    uint64_t magic;
+    Kind kind;
+    union {
+        LayoutArgs layout;
+        DispatchArgs dispatch;
+        LayoutDispatchArgs layout_dispatch;
+        CombineArgs combine;
+    };
+};
+static_assert(sizeof(PlanRecord) <= sizeof(moe_plan), "moe_plan is too small for a plan record");
+static_assert(std::is_trivially_copyable<PlanRecord>::value, "plan records are copied as bytes");
+
+// Stores rec in plan when st is MOE_OK; otherwise clears the plan (moe_plan_run then refuses it).
+int store_plan(moe_plan *plan, PlanRecord &rec, int st) {
+    std::memset(plan, 0, sizeof(*plan));
+    if (st != MOE_OK) return st;
+    rec.magic = PlanRecord::kMagic;
+    std::memcpy(plan, &rec, sizeof(rec));
+    return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int64_t moe_slot_bytes(int32_t H) {
@@ -122,31 +291,11 @@ int moe_layout_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int3
                   int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
                   int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t path,
                   hipStream_t stream) {
-    if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
-        !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
-        !slot_idx || !status)
-        return MOE_ERR_ARG;
-    int st = check_tokens(S, K);
-    if (st != MOE_OK) return st;
-    if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
-    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
-    if (E % P != 0) return MOE_ERR_UNSUPPORTED;
-    const int form = pick_layout(path, S, K, E, P, C);
-    if (form < 0) return MOE_ERR_ARG;
-    if (form == 2) return MOE_ERR_UNSUPPORTED;
-    const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
-                         expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
-    for (const void *p : i32)
-        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
-    if (form == 1)
-        return from_hip(moe::launch_layout_small(
-            topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
-            rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
-            status, stream));
-    return from_hip(moe::launch_layout(topk_idx, S, K, E, P, C, is_token_in_rank,
-                                       num_tokens_per_rank, num_tokens_per_expert,
-                                       rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
-                                       expert_slot_base, slot_idx, status, stream));
+    LayoutArgs a{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                 num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
+                 expert_slot_base, slot_idx, status, 0};
+    const int st = check_layout(a, path);
+    return st != MOE_OK ? st : run_layout(a, stream);
 }
 
 int moe_layout(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
@@ -178,16 +327,9 @@ int64_t moe_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t quant) {
 int moe_dispatch_ws(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                     int32_t quant, int32_t src_rank, void *window, int64_t window_bytes,
                     void *workspace, int64_t workspace_bytes, hipStream_t stream) {
-    const int st = moe::check_dispatch(x, slot_idx, S, H, K, quant, window, window_bytes);
-    if (st != MOE_OK) return st;
-    const bool planned = moe::pack_planned_used(S, K, quant);
-    if (planned && !workspace) return MOE_ERR_ARG;
-    if (planned && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
-    if (planned && workspace_bytes < moe::pack_plan_bytes(S, K)) return MOE_ERR_WINDOW;
-    if (planned)
-        return from_hip(moe::launch_pack_planned(x, slot_idx, S, H, K, src_rank, window, workspace,
-                                                 stream));
-    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+    DispatchArgs a{x, slot_idx, S, H, K, quant, src_rank, window, workspace, false};
+    const int st = check_dispatch_ws(a, window_bytes, workspace_bytes);
+    return st != MOE_OK ? st : run_dispatch_ws(a, stream);
 }
 
 int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
@@ -197,38 +339,12 @@ int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_
                            int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
                            const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
                            int64_t window_bytes, int32_t path, hipStream_t stream) {
-    if (!topk_idx || !is_token_in_rank || !num_tokens_per_rank || !num_tokens_per_expert ||
-        !rank_prefix_matrix || !expert_prefix_matrix || !rank_slot_base || !expert_slot_base ||
-        !slot_idx || !status || !x || !window)
-        return MOE_ERR_ARG;
-    int st = check_tokens(S, K);
-    if (st != MOE_OK) return st;
-    if (E < 1 || E > MOE_MAX_EXPERTS || P < 1 || P > MOE_MAX_RANKS) return MOE_ERR_ARG;
-    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
-    st = check_hidden(H);
-    if (st != MOE_OK) return st;
-    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
-    if (E % P != 0) return MOE_ERR_UNSUPPORTED;
-    const int form = pick_layout(path, S, K, E, P, C);
-    if (form < 0) return MOE_ERR_ARG;
-    if (form == 2) return MOE_ERR_UNSUPPORTED;
-    const void *i32[] = {topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
-                         expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx, status};
-    for (const void *p : i32)
-        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
-    if (!aligned(x, 16) || !aligned(window, 512)) return MOE_ERR_ALIGN;
-    if (window_bytes < moe_window_bytes(S, K, H)) return MOE_ERR_WINDOW;
-    if (form == 1)
-        return from_hip(moe::launch_layout_dispatch_small(
-            topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
-            rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
-            status, x, H, quant, src_rank, window, stream));
-    st = from_hip(moe::launch_layout(topk_idx, S, K, E, P, C, is_token_in_rank,
-                                     num_tokens_per_rank, num_tokens_per_expert,
-                                     rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
-                                     expert_slot_base, slot_idx, status, stream));
-    if (st != MOE_OK) return st;
-    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+    LayoutDispatchArgs a{{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                          num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                          rank_slot_base, expert_slot_base, slot_idx, status, 0},
+                         x, H, quant, src_rank, window};
+    const int st = check_layout_dispatch(a, path, window_bytes);
+    return st != MOE_OK ? st : run_layout_dispatch(a, stream);
 }
 
 int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
@@ -247,18 +363,78 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                 const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
                 int32_t K, void *y, hipStream_t stream) {
-    if (!expert_out || !slot_idx || !topk_weights || !y) return MOE_ERR_ARG;
-    int st = check_tokens(S, K);
-    if (st != MOE_OK) return st;
-    st = check_hidden(H);
-    if (st != MOE_OK) return st;
-    if (expert_rows < 0 || row_stride_bytes < 2 * (int64_t)H) return MOE_ERR_ARG;
-    if (!extent_fits(expert_rows, row_stride_bytes)) return MOE_ERR_ARG;
-    if (row_stride_bytes % 16 != 0 || !aligned(expert_out, 16) || !aligned(y, 16) ||
-        !aligned(slot_idx, 4) || !aligned(topk_weights, 4))
-        return MOE_ERR_ALIGN;
-    return from_hip(moe::launch_combine(expert_out, row_stride_bytes, expert_rows, slot_idx,
-                                        topk_weights, S, H, K, y, stream));
+    CombineArgs a{expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights, S, H, K, y};
+    const int st = check_combine(a);
+    return st != MOE_OK ? st : run_combine(a, stream);
+}
+
+// ---- pre-validated calls (moe_plan_*): the checks above run once, moe_plan_run only launches
+
+int moe_plan_layout(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K, int32_t E,
+                    int32_t P, int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                    int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                    int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                    int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t path) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kLayout;
+    rec.layout = LayoutArgs{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                            num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                            rank_slot_base, expert_slot_base, slot_idx, status, 0};
+    return store_plan(plan, rec, check_layout(rec.layout, path));
+}
+
+int moe_plan_dispatch_ws(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
+                         int32_t H, int32_t K, int32_t quant, int32_t src_rank, void *window,
+                         int64_t window_bytes, void *workspace, int64_t workspace_bytes) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kDispatch;
+    rec.dispatch = DispatchArgs{x, slot_idx, S, H, K, quant, src_rank, window, workspace, false};
+    return store_plan(plan, rec, check_dispatch_ws(rec.dispatch, window_bytes, workspace_bytes));
+}
+
+int moe_plan_layout_dispatch(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K,
+                             int32_t E, int32_t P, int32_t C, uint8_t *is_token_in_rank,
+                             int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                             int32_t *rank_prefix_matrix, int32_t *expert_prefix_matrix,
+                             int32_t *rank_slot_base, int32_t *expert_slot_base, int32_t *slot_idx,
+                             int32_t *status, const void *x, int32_t H, int32_t quant,
+                             int32_t src_rank, void *window, int64_t window_bytes, int32_t path) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kLayoutDispatch;
+    rec.layout_dispatch = LayoutDispatchArgs{
+        {topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank, num_tokens_per_expert,
+         rank_prefix_matrix, expert_prefix_matrix, rank_slot_base, expert_slot_base, slot_idx,
+         status, 0},
+        x, H, quant, src_rank, window};
+    return store_plan(plan, rec, check_layout_dispatch(rec.layout_dispatch, path, window_bytes));
+}
+
+int moe_plan_combine(moe_plan *plan, const void *expert_out, int64_t row_stride_bytes,
+                     int64_t expert_rows, const int32_t *slot_idx, const float *topk_weights,
+                     int32_t S, int32_t H, int32_t K, void *y) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kCombine;
+    rec.combine = CombineArgs{expert_out, row_stride_bytes, expert_rows, slot_idx, topk_weights,
+                              S, H, K, y};
+    return store_plan(plan, rec, check_combine(rec.combine));
+}
+
+int moe_plan_run(const moe_plan *plan, hipStream_t stream) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec;
+    std::memcpy(&rec, plan, sizeof(rec));
+    if (rec.magic != PlanRecord::kMagic) return MOE_ERR_ARG;
+    switch (rec.kind) {
+        case PlanRecord::kLayout: return run_layout(rec.layout, stream);
+        case PlanRecord::kDispatch: return run_dispatch_ws(rec.dispatch, stream);
+        case PlanRecord::kLayoutDispatch: return run_layout_dispatch(rec.layout_dispatch, stream);
+        case PlanRecord::kCombine: return run_combine(rec.combine, stream);
+        default: return MOE_ERR_ARG;
+    }
 }
 
 int moe_combine_scatter(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,

@@ -394,6 +394,48 @@ int moe_unpack_padded(const void *window, int64_t window_bytes, const int32_t *e
                       float *expand_scales, int32_t *expand_idx, int32_t *expert_row_base,
                       int32_t *status, hipStream_t stream);
 
+/* Pre-validated calls, for callers that launch the same calls on the same buffers again and again
+ * (a decode loop; "Ascend DeepEP MoE Dispatch Optimization", section "从 Python 接口进入真实调用链"
+ * shows how much of a small dispatch's time goes to the host side of the call). moe_plan_* takes
+ * the arguments of the call it names (without the stream), runs exactly that call's checks and, if
+ * they pass, records the arguments in *plan and returns MOE_OK; otherwise it returns the call's
+ * error and leaves *plan cleared. moe_plan_run(plan, stream) then enqueues the call's kernels on
+ * stream without checking anything again, exactly as the direct call would: the buffers the plan
+ * names must stay allocated and keep their sizes while the plan is in use. A plan is plain
+ * caller-owned memory (no handle, nothing to free) and may be copied; moe_plan_run refuses
+ * (MOE_ERR_ARG) a plan that no moe_plan_* call filled.
+ *   moe_plan_layout           -> moe_layout_ex (path as there)
+ *   moe_plan_dispatch_ws      -> moe_dispatch_ws
+ *   moe_plan_layout_dispatch  -> moe_layout_dispatch_ex (path as there)
+ *   moe_plan_combine          -> moe_combine */
+typedef struct {
+    uint64_t opaque[40];
+} moe_plan;
+
+int moe_plan_layout(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K, int32_t E,
+                    int32_t P, int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                    int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                    int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                    int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t path);
+
+int moe_plan_dispatch_ws(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
+                         int32_t H, int32_t K, int32_t quant, int32_t src_rank, void *window,
+                         int64_t window_bytes, void *workspace, int64_t workspace_bytes);
+
+int moe_plan_layout_dispatch(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K,
+                             int32_t E, int32_t P, int32_t C, uint8_t *is_token_in_rank,
+                             int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                             int32_t *rank_prefix_matrix, int32_t *expert_prefix_matrix,
+                             int32_t *rank_slot_base, int32_t *expert_slot_base, int32_t *slot_idx,
+                             int32_t *status, const void *x, int32_t H, int32_t quant,
+                             int32_t src_rank, void *window, int64_t window_bytes, int32_t path);
+
+int moe_plan_combine(moe_plan *plan, const void *expert_out, int64_t row_stride_bytes,
+                     int64_t expert_rows, const int32_t *slot_idx, const float *topk_weights,
+                     int32_t S, int32_t H, int32_t K, void *y);
+
+int moe_plan_run(const moe_plan *plan, hipStream_t stream);
+
 /* Static description of a moe_status value (never NULL). */
 const char *moe_status_string(int status);
 

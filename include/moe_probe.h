@@ -2,8 +2,8 @@
  * moe_probe.h - bandwidth probes of libmoe.so, for measurement only (not part of the hot path).
  *
  * The practical HBM ceilings of the three access patterns the path's kernels mix, measured on the
- * running GPU with the same cache policies as those kernels (16-byte buffer loads with the default
- * policy, 16-byte streaming stores): a write-only fill, a read-only stream and a copy. The bench
+ * running GPU with the cache policies of those kernels (16-byte buffer loads with the nt policy of
+ * data read once, 16-byte streaming stores): a write-only fill, a read-only stream and a copy. The bench
  * reports each kernel's bandwidth against the ceiling of its own read/write mix next to the
  * specification peak ("Ascend DeepEP MoE Dispatch Optimization", section "结论": the pages measure
  * dispatch against the hardware's theoretical bandwidth).

@@ -242,6 +242,45 @@ int main() {
                only(stubs::kExpandDedup, 1),
            "expand_dedup");
 
+    // pre-validated calls reach the same launchers as the direct calls
+    {
+        moe_plan plan;
+        stubs::reset();
+        expect(moe_plan_layout(&plan, I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_AUTO) == MOE_OK &&
+                   only(stubs::kLaunchers, 0),
+               "plan_layout checks without launching");
+        expect(moe_plan_run(&plan, nullptr) == MOE_OK && only(stubs::kLayoutSmall, 1), "plan_run layout small");
+        stubs::reset();
+        expect(moe_plan_layout(&plan, I, 513, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, MOE_LAYOUT_AUTO) == MOE_OK &&
+                   moe_plan_run(&plan, nullptr) == MOE_OK && only(stubs::kLayout, 1),
+               "plan_run layout multi");
+        stubs::reset();
+        expect(moe_plan_layout_dispatch(&plan, I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 1, 0, A,
+                                        win, MOE_LAYOUT_AUTO) == MOE_OK &&
+                   moe_plan_run(&plan, nullptr) == MOE_OK && moe_plan_run(&plan, nullptr) == MOE_OK &&
+                   only(stubs::kLayoutDispatchSmall, 2),
+               "plan_run layout_dispatch twice -> one kernel each");
+        stubs::reset();
+        expect(moe_plan_layout_dispatch(&plan, I, 513, 8, 256, 8, 128, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A,
+                                        moe_window_bytes(513, 8, 7168), MOE_LAYOUT_AUTO) == MOE_OK &&
+                   moe_plan_run(&plan, nullptr) == MOE_OK && only(stubs::kLayout, 1, stubs::kPack, 1),
+               "plan_run layout_dispatch large -> layout + pack");
+        const int64_t wbig = moe_window_bytes(4096, 8, 7168);
+        stubs::reset();
+        expect(moe_plan_dispatch_ws(&plan, A, I, 4096, 7168, 8, 0, 0, A, wbig, A,
+                                    moe_dispatch_workspace_bytes(4096, 8, 0)) == MOE_OK &&
+                   moe_plan_run(&plan, nullptr) == MOE_OK && only(stubs::kPackPlanned, 1),
+               "plan_run dispatch_ws -> planned pack");
+        stubs::reset();
+        expect(moe_plan_combine(&plan, A, 14848, 512, I, F, 64, 7168, 8, A) == MOE_OK &&
+                   moe_plan_run(&plan, nullptr) == MOE_OK && only(stubs::kCombine, 1),
+               "plan_run combine");
+        stubs::reset();
+        expect(moe_plan_combine(&plan, A, 100, 512, I, F, 64, 7168, 8, A) == MOE_ERR_ARG &&
+                   moe_plan_run(&plan, nullptr) == MOE_ERR_ARG && only(stubs::kLaunchers, 0),
+               "a failed plan cannot be run");
+    }
+
     if (failures == 0) std::printf("abi_asan ok\n");
     return failures == 0 ? 0 : 1;
 }

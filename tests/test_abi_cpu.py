@@ -186,6 +186,38 @@ def test_noalloc_rejects_tables_beyond_its_scratch():
     assert "scratch" in moe.moe_status_string(moe.MOE_ERR_SCRATCH)
 
 
+def test_plan_size_matches_the_header():
+    text = open(HEADER, encoding="utf-8").read()
+    words = int(re.search(r"uint64_t opaque\[(\d+)\];", text).group(1))
+    assert moe.MOE_PLAN_BYTES == 8 * words
+
+
+def test_plans_check_like_the_calls_and_refuse_unfilled_plans():
+    """Each moe_plan_* returns the error of the call it stands for and leaves the plan cleared, so
+    moe_plan_run refuses it (no HIP call is made on these paths)."""
+    lib = moe._lib
+    buf = ctypes.create_string_buffer(moe.MOE_PLAN_BYTES)
+    addr = ctypes.addressof(buf)
+    assert lib.moe_plan_run(addr, None) == moe.MOE_ERR_ARG  # never filled
+    assert lib.moe_plan_run(None, None) == moe.MOE_ERR_ARG
+    outs = [A] * 9
+    assert lib.moe_plan_layout(addr, A, 64, 8, 250, 8, 16, *outs, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_layout(addr, A, 64, 8, 256, 8, 65, *outs, 0) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_layout(addr, A, 513, 8, 256, 8, 16, *outs, moe.MOE_LAYOUT_SINGLE) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_run(addr, None) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_dispatch_ws(addr, A, A, 4096, 7168, 8, 0, 0, A, 4096 * 8 * 14848, NULL, 0) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_dispatch_ws(addr, A, A, 64, 7168, 8, 0, 0, A, 10, NULL, 0) == moe.MOE_ERR_WINDOW
+    assert lib.moe_plan_layout_dispatch(addr, A, 64, 8, 256, 8, 16, *outs, A, 7168, 0, 0, A, 0, 0) == \
+        moe.MOE_ERR_WINDOW
+    assert lib.moe_plan_layout_dispatch(addr, A, 64, 8, 256, 8, 16, *outs, A + 8, 7168, 0, 0, A,
+                                        64 * 8 * 14848, 0) == moe.MOE_ERR_ALIGN
+    assert lib.moe_plan_combine(addr, A, 14000, 512, A, A, 64, 7168, 8, A) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_combine(addr, A, 14336, 512, A, A, 64, 7168, 8, A + 8) == moe.MOE_ERR_ALIGN
+    assert lib.moe_plan_combine(None, A, 14336, 512, A, A, 64, 7168, 8, A) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_run(addr, None) == moe.MOE_ERR_ARG
+    assert buf.raw == bytes(moe.MOE_PLAN_BYTES)  # cleared after every failed check
+
+
 def layout_dispatch_call(topk=A, S=64, K=8, E=256, P=8, C=16, outs=None, x=A, H=7168, quant=0,
                          window=A, nbytes=None):
     outs = outs if outs is not None else [A] * 9

@@ -1125,6 +1125,50 @@ def test_maximum_tokens_and_channels(moe):
     assert np.array_equal(y, oracle.combine(rows, ref["slot_idx"], wts))
 
 
+@pytest.mark.parametrize("cfg,quant,fused", [(2, 0, True), (2, 1, True), (1, 2, True), (3, 0, False)])
+def test_plans_match_the_oracle(moe, cfg, quant, fused):
+    """Pre-validated calls (moe_plan_*, run by moe_plan_run) on fixed buffers, three seeded inputs
+    copied into them one after the other: layout, window and y against the oracle each time."""
+    w = WORKLOADS[cfg]
+    S, K, H, E, P, C = w.S, w.K, w.H, w.E, w.P, w.C
+    idx_s = torch.empty((S, K), dtype=torch.int32, device=DEV)
+    x_s = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+    eo_s = torch.empty((S * K, H), dtype=torch.bfloat16, device=DEV)
+    wts_s = torch.empty((S, K), dtype=torch.float32, device=DEV)
+    lay = moe.empty_layout(S, K, E, P, C, DEV)
+    win = torch.empty(moe.moe_window_bytes(S, K, H), dtype=torch.uint8, device=DEV)
+    y = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+    nws = moe.moe_dispatch_workspace_bytes(S, K, quant)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV) if nws else None
+    if fused:
+        plans = [moe.plan_layout_dispatch(idx_s, E, P, C, x_s, win, lay, quant, 6)]
+    else:
+        plans = [moe.plan_layout(idx_s, E, P, C, lay), moe.plan_dispatch_ws(x_s, lay.slot_idx, win, ws, quant, 6)]
+    plans.append(moe.plan_combine(eo_s, lay.slot_idx, wts_s, y))
+    for seed in (1, 2, 3):
+        rng = np.random.default_rng(1000 * cfg + seed)
+        idx = random_tiny_routing(rng, S, K, E, p_mask=0.05, p_bad=0.01)
+        x = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+        eo = f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))
+        wts = rng.random((S, K)).astype(np.float32)
+        idx_s.copy_(to_dev(idx))
+        x_s.copy_(bf16_dev(x))
+        eo_s.copy_(bf16_dev(eo))
+        wts_s.copy_(to_dev(wts))
+        win.fill_(POISON)
+        torch.cuda.synchronize()
+        for plan in plans:
+            plan.run()
+        torch.cuda.synchronize()
+        note(f"plans cfg{cfg} quant {quant} fused {fused} seed {seed}")
+        ref = oracle.layout(idx, E, P, C)
+        assert_layout_equal({k: v.cpu().numpy() for k, v in lay._asdict().items()}, ref, f"plan seed {seed}")
+        assert_window_equal(win.cpu().numpy().reshape(S * K, -1), oracle.dispatch_slots(x, ref["slot_idx"], quant, 6),
+                            oracle.slot_geometry(H, quant), f"plan seed {seed}")
+        got_y = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_y, oracle.combine(eo, ref["slot_idx"], wts)), f"plan seed {seed}"
+
+
 def test_python_layer_rejects_bad_window(moe):
     x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
     slot = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
