@@ -1,15 +1,18 @@
 """Benchmark of the MoE normal-mode hot path on one MI355X.
 
-One step = moe_layout + moe_dispatch + moe_combine over one batch of seeded
+One step = layout + dispatch + combine over one batch of seeded
 synthetic input already resident in HBM (default: the DeepSeek-V3-shaped
 prefill, S=4096 H=7168 E=256 P=8 K=8, bf16). Prints ONE JSON line with the
 whole-step throughput in GB/s of algorithmic bytes, tokens/s, per-kernel event
 timings, the roofline of the dominant kernel and the CPU oracle timed on the
 host cores as a reported baseline.
 
-The dispatch is moe_dispatch_ws (the planned pack with its workspace: a plan
-kernel, then the pack kernel; the token-order moe_dispatch is timed beside it in
-extras.dispatch_token_order).
+The layout is moe_layout_ws (two kernels; in bf16 the second also writes the
+pack's plan into the workspace) and the dispatch moe_dispatch_planned (the
+planned pack kernel alone, reading that plan). extras.three_launch_layout_dispatch_ws
+times the step with moe_layout (three kernels) + moe_dispatch_ws (plan kernel +
+pack kernel), and the token-order moe_dispatch is timed in
+extras.dispatch_token_order.
 
 Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
 at distinct addresses, so each step reads its inputs from HBM rather than from
@@ -31,7 +34,7 @@ puts 16 steps in one graph so that the replay's own launch cost is shared.
 Timing: value and ms_per_step come from the K timed steps with nothing recorded
 between the kernels (wall clock between two device synchronisations). The same
 K steps then run again with an event before and after every call; kernels
-holds those event statistics per call (layout, dispatch = plan + pack, combine)
+holds those event statistics per call (layout, dispatch = the pack kernel, combine)
 and for the sums layout+dispatch and layout+dispatch+combine, each with its
 bytes, GB/s, fraction of 8 TB/s, tokens/s and fraction of its pattern ceiling.
 Each event adds a few microseconds to the interval it bounds, so the event
@@ -222,7 +225,28 @@ def time_fused_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
-def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes, ws):
+def time_three_launch_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes, ws):
+    """The step with moe_layout (three kernels) and moe_dispatch_ws (plan kernel + pack kernel), launched
+    eagerly like the timed steps."""
+    def step(i):
+        x, topk, wts, eo = sets[i % len(sets)]
+        moe.moe_layout(topk, w.E, w.P, C, out=lay)
+        moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
+
+
+def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes, lws):
     """The step through pre-validated calls (moe_plan_*): one plan per input set made once, then each
     step runs its plans (moe_plan_run: one short C call per launch, no argument checks), launched
     eagerly like the timed steps."""
@@ -231,8 +255,8 @@ def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes
         if w.S * w.K <= 4096 and C <= 1024:  # decode sizes: layout + pack in one kernel
             first = [moe.plan_layout_dispatch(topk, w.E, w.P, C, x, window, lay, w.quant, 0)]
         else:
-            first = [moe.plan_layout(topk, w.E, w.P, C, lay), moe.plan_dispatch_ws(x, lay.slot_idx, window, ws,
-                                                                                     w.quant, 0)]
+            first = [moe.plan_layout_ws(topk, w.E, w.P, C, lay, lws, w.quant),
+                     moe.plan_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)]
         plans.append([p.run for p in first] + [moe.plan_combine(eo, lay.slot_idx, wts, y).run])
     n = len(plans)
     for i in range(args.warmup):
@@ -250,7 +274,7 @@ def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes
 
 
 def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1,
-                      ws=None):
+                      lws=None):
     """The same step captured in HIP graphs and replayed: the device time of a step without the
     Python launch overhead, which dominates at decode sizes. per_graph = 1: one graph per input set,
     one step per replay; per_graph > 1: that many steps (cycling over the input sets) in one graph,
@@ -260,8 +284,8 @@ def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
         if fused:
             moe.moe_layout_dispatch(topk, w.E, w.P, C, x, window, w.quant, 0, out=lay)
         else:
-            moe.moe_layout(topk, w.E, w.P, C, out=lay)
-            moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
+            moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
+            moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
     graphs = []
@@ -503,6 +527,8 @@ def main():
     window = torch.empty(moe.moe_window_bytes(w.S, w.K, w.H), dtype=torch.uint8, device=dev)
     nws = moe.moe_dispatch_workspace_bytes(w.S, w.K, w.quant)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    nlws = moe.moe_layout_dispatch_workspace_bytes(w.S, w.K, w.E, w.P, C, w.quant)
+    lws = torch.empty(nlws, dtype=torch.uint8, device=dev) if nlws else None
     y = torch.empty((w.S, w.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -517,8 +543,8 @@ def main():
 
     def step(i, sets_used):
         x, topk, wts, eo = sets_used[i % len(sets_used)]
-        moe.moe_layout(topk, w.E, w.P, C, out=lay)
-        moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
+        moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
+        moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
         moe.moe_combine(eo, lay.slot_idx, wts, y=y)
 
     def timed(sets_used):
@@ -541,9 +567,9 @@ def main():
             e = ev[i]
             x, topk, wts, eo = sets_used[i % len(sets_used)]
             e[0].record(stream)
-            moe.moe_layout(topk, w.E, w.P, C, out=lay)
+            moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
             e[1].record(stream)
-            moe.moe_dispatch_ws(x, lay.slot_idx, window, ws, w.quant, 0)
+            moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
             e[2].record(stream)
             moe.moe_combine(eo, lay.slot_idx, wts, y=y)
             e[3].record(stream)
@@ -601,8 +627,8 @@ def main():
         return out
 
     calls = {
-        "layout": lambda st: moe.moe_layout(st[1], w.E, w.P, C, out=lay),
-        "dispatch": lambda st: moe.moe_dispatch_ws(st[0], lay.slot_idx, window, ws, w.quant, 0),
+        "layout": lambda st: moe.moe_layout_ws(st[1], w.E, w.P, C, lws, w.quant, out=lay),
+        "dispatch": lambda st: moe.moe_dispatch_planned(st[0], lay.slot_idx, window, lws, C, w.quant, 0),
         "combine": lambda st: moe.moe_combine(st[3], lay.slot_idx, st[2], y=y),
     }
 
@@ -624,14 +650,15 @@ def main():
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: kernels[k]["avg_us"])
     planned = moe.moe_dispatch_workspace_bytes(w.S, w.K, w.quant) > 0
+    plan_by_layout = planned and -(-w.S // C) * w.K <= 1024  # else moe_dispatch_planned runs the plan kernel
     kernel_key = {"dispatch": {0: "pack_bf16_planned" if planned else "pack_bf16", 1: "pack_fp8",
                                2: "pack_int8"}[w.quant],
                   "combine": "combine"}[dom]
     traffic = traffic_from_profiles(f"{kernel_key}:{w.name}")
     roofline = {
         "bound": "hbm", "kernel": kernel_key,
-        "launches": ("plan + pack kernels of one moe_dispatch_ws call" if dom == "dispatch" and planned
-                     else "one kernel"),
+        "launches": ("plan + pack kernels of one moe_dispatch_planned call" if dom == "dispatch" and planned
+                     and not plan_by_layout else "one kernel"),
         "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(kernels[dom]["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
         "algorithmic_bytes_per_launch": nbytes[dom],
@@ -679,17 +706,19 @@ def main():
                 "kernels": {k: {f: v[f] for f in ("avg_us", "GB/s", "frac_hbm_peak")} for k, v in warm.items()}}
         out["extras"]["fused_layout_dispatch"] = time_fused_eager(args, torch, moe, w, C, sets, lay, window,
                                                                   y, total_bytes)
+        out["extras"]["three_launch_layout_dispatch_ws"] = time_three_launch_eager(
+            args, torch, moe, w, C, sets, lay, window, y, total_bytes, ws)
         out["extras"]["planned_calls_eager"] = time_planned_eager(args, torch, moe, w, C, sets, lay, window, y,
-                                                                  total_bytes, ws)
+                                                                  total_bytes, lws)
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
-                                                          total_bytes, ws=ws)
+                                                          total_bytes, lws=lws)
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
         fused["one_kernel_layout_dispatch"] = w.S * w.K <= 4096 and C <= 1024
         out["extras"]["graph_replay_fused_layout_dispatch"] = fused
         if w.S * w.K <= 4096:  # decode sizes: 16 steps per graph, the replay's own cost shared
             out["extras"]["graph_replay_16_steps_per_graph"] = {
                 "separate": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
-                                              per_graph=16, ws=ws),
+                                              per_graph=16, lws=lws),
                 "fused_layout_dispatch": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                            total_bytes, fused=True, per_graph=16)}
         if w.name == "dsv3_prefill":

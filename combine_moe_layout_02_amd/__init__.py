@@ -37,10 +37,11 @@ MOE_LAYOUT_SINGLE = 2
 EXPORTED = (
     "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout", "moe_layout_ex", "moe_dispatch",
     "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc",
-    "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
+    "moe_layout_dispatch", "moe_layout_dispatch_ex", "moe_layout_dispatch_workspace_bytes",
+    "moe_layout_ws", "moe_dispatch_planned", "moe_layout_dispatch_ws", "moe_combine", "moe_combine_scatter", "moe_combine_staged",
     "moe_unpack", "moe_unpack_padded", "moe_dedup_window_bytes", "moe_rank_rows", "moe_dispatch_dedup",
     "moe_expand_dedup", "moe_status_string", "moe_plan_layout", "moe_plan_dispatch_ws",
-    "moe_plan_layout_dispatch", "moe_plan_combine", "moe_plan_run",
+    "moe_plan_layout_dispatch", "moe_plan_combine", "moe_plan_layout_ws", "moe_plan_dispatch_planned", "moe_plan_run",
 )
 
 # include/moe_probe.h: bandwidth probes for the measurement, not part of the path
@@ -73,6 +74,11 @@ def _load():
                                 [P, I32, I32, I32, P, I64, P]),
         "moe_layout_dispatch_ex": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
                                    [P, I32, I32, I32, P, I64, I32, P]),
+        "moe_layout_dispatch_workspace_bytes": (I64, [I32, I32, I32, I32, I32, I32, I32]),
+        "moe_layout_ws": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 + [I32, I32, P, I64, P]),
+        "moe_dispatch_planned": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, I32, P, I64, P, I64, P]),
+        "moe_layout_dispatch_ws": (ctypes.c_int, [P, I32, I32, I32, I32, I32] + [P] * 9 +
+                                   [P, I32, I32, I32, P, I64, I32, P, I64, P]),
         "moe_combine": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
         "moe_combine_scatter": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, I64, I64, P]),
         "moe_combine_staged": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I32, P, P]),
@@ -86,6 +92,8 @@ def _load():
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_plan_layout": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32] + [P] * 9 + [I32]),
         "moe_plan_dispatch_ws": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, P, I64, P, I64]),
+        "moe_plan_layout_ws": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32] + [P] * 9 + [I32, I32, P, I64]),
+        "moe_plan_dispatch_planned": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, I64]),
         "moe_plan_layout_dispatch": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32] + [P] * 9 +
                                      [P, I32, I32, I32, P, I64, I32]),
         "moe_plan_combine": (ctypes.c_int, [P, P, I64, I64, P, P, I32, I32, I32, P]),
@@ -317,6 +325,79 @@ def moe_layout_dispatch(topk_idx, num_experts, num_ranks, num_channels, x, windo
     return out
 
 
+def moe_layout_dispatch_workspace_bytes(S, K, E, P, C, quant=MOE_QUANT_NONE, path=MOE_LAYOUT_AUTO):
+    v = _lib.moe_layout_dispatch_workspace_bytes(int(S), int(K), int(E), int(P), int(C), int(quant), int(path))
+    if v < 0:
+        _check(int(v))
+    return int(v)
+
+
+def _ws_arg(workspace, dev):
+    if workspace is None:
+        return None, 0
+    _need(workspace, "workspace", device=dev)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def moe_layout_ws(topk_idx, num_experts, num_ranks, num_channels, workspace, quant=MOE_QUANT_NONE,
+                  out=None, stream=None, path=MOE_LAYOUT_AUTO):
+    """moe_layout with a caller workspace (moe_layout_dispatch_workspace_bytes(...) bytes, or None when
+    that is 0): two kernels, and in bf16 the pack plan for moe_dispatch_planned."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    dev = topk_idx.device
+    S, K = topk_idx.shape
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    if out is None:
+        out = empty_layout(S, K, E, P, C, dev)
+    _need_layout(out, S, K, E, P, C, dev)
+    ws_ptr, ws_bytes = _ws_arg(workspace, dev)
+    _check(_lib.moe_layout_ws(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out], int(quant), int(path),
+                              ws_ptr, ws_bytes, _stream(dev, stream)))
+    return out
+
+
+def moe_dispatch_planned(x, slot_idx, window, workspace, num_channels, quant=MOE_QUANT_NONE, src_rank=0,
+                         stream=None):
+    """The pack of the table moe_layout_ws just laid out, from the plan it left in `workspace`."""
+    _need(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _need(slot_idx, "slot_idx", torch.int32, 2, dev)
+    _need(window, "window", device=dev)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    ws_ptr, ws_bytes = _ws_arg(workspace, dev)
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_dispatch_planned(_ptr(x), _ptr(slot_idx), S, H, K, int(num_channels), int(quant),
+                                     int(src_rank), _ptr(window), nbytes, ws_ptr, ws_bytes, _stream(dev, stream)))
+    return window
+
+
+def moe_layout_dispatch_ws(topk_idx, num_experts, num_ranks, num_channels, x, window, workspace,
+                           quant=MOE_QUANT_NONE, src_rank=0, out=None, stream=None, path=MOE_LAYOUT_AUTO):
+    """moe_layout_dispatch with a caller workspace (at least moe_layout_dispatch_workspace_bytes(...)
+    bytes, or None when that size is 0): two layout kernels, the pack plan written by the layout."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    dev = topk_idx.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(window, "window", device=dev)
+    S, K = topk_idx.shape
+    if x.shape[0] != S:
+        raise ValueError("x must have one row per token of topk_idx")
+    H = x.shape[1]
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    if out is None:
+        out = empty_layout(S, K, E, P, C, dev)
+    _need_layout(out, S, K, E, P, C, dev)
+    ws_ptr, ws_bytes = _ws_arg(workspace, dev)
+    nbytes = window.numel() * window.element_size()
+    _check(_lib.moe_layout_dispatch_ws(_ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out], _ptr(x), H,
+                                       int(quant), int(src_rank), _ptr(window), nbytes, int(path), ws_ptr,
+                                       ws_bytes, _stream(dev, stream)))
+    return out
+
+
 def moe_combine(expert_out, slot_idx, topk_weights, row_stride_bytes=None, expert_rows=None,
                 hidden=None, y=None, stream=None):
     """y[t] = bf16(sum_k w[t,k] * expert_out[slot_idx[t,k]]) with fp32 accumulation.
@@ -482,6 +563,38 @@ def plan_dispatch_ws(x, slot_idx, window, workspace, quant=MOE_QUANT_NONE, src_r
     plan = Plan(x.device, (x, slot_idx, window, workspace))
     _check(_lib.moe_plan_dispatch_ws(plan._addr, _ptr(x), _ptr(slot_idx), S, H, K, int(quant), int(src_rank),
                                      _ptr(window), window.numel() * window.element_size(), ws_ptr, ws_bytes))
+    return plan
+
+
+def plan_layout_ws(topk_idx, num_experts, num_ranks, num_channels, out, workspace, quant=MOE_QUANT_NONE,
+                   path=MOE_LAYOUT_AUTO):
+    """Plan of moe_layout_ws on these buffers (out: a Layout)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    S, K = topk_idx.shape
+    E, P, C = int(num_experts), int(num_ranks), int(num_channels)
+    dev = topk_idx.device
+    _need_layout(out, S, K, E, P, C, dev)
+    ws_ptr, ws_bytes = _ws_arg(workspace, dev)
+    plan = Plan(dev, (topk_idx, out, workspace))
+    _check(_lib.moe_plan_layout_ws(plan._addr, _ptr(topk_idx), S, K, E, P, C, *[_ptr(t) for t in out], int(quant),
+                                   int(path), ws_ptr, ws_bytes))
+    return plan
+
+
+def plan_dispatch_planned(x, slot_idx, window, workspace, num_channels, quant=MOE_QUANT_NONE, src_rank=0):
+    """Plan of moe_dispatch_planned on these buffers."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 2, x.device)
+    _need(window, "window", device=x.device)
+    S, H = x.shape
+    if slot_idx.shape[0] != S:
+        raise ValueError("slot_idx must have one row per token of x")
+    K = slot_idx.shape[1]
+    ws_ptr, ws_bytes = _ws_arg(workspace, x.device)
+    plan = Plan(x.device, (x, slot_idx, window, workspace))
+    _check(_lib.moe_plan_dispatch_planned(plan._addr, _ptr(x), _ptr(slot_idx), S, H, K, int(num_channels), int(quant),
+                                          int(src_rank), _ptr(window), window.numel() * window.element_size(),
+                                          ws_ptr, ws_bytes))
     return plan
 
 
@@ -711,8 +824,10 @@ __all__ = [
     "MOE_LAYOUT_MULTI", "MOE_LAYOUT_SINGLE", "MoeError", "Layout",
     "empty_layout", "moe_slot_bytes", "moe_window_bytes", "moe_slot_offsets", "moe_layout",
     "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_dispatch_ws", "moe_dispatch_noalloc", "MOE_ERR_SCRATCH",
+    "moe_layout_dispatch_workspace_bytes", "moe_layout_ws", "moe_dispatch_planned", "moe_layout_dispatch_ws",
     "MOE_NOALLOC_SCRATCH_BYTES", "moe_layout_dispatch", "moe_combine", "moe_combine_scatter", "moe_combine_staged", "moe_unpack", "Unpacked", "moe_unpack_padded", "PaddedUnpacked",
     "moe_dedup_window_bytes", "moe_rank_rows", "RankRows", "moe_dispatch_dedup", "moe_expand_dedup",
     "moe_status_string", "Plan", "plan_layout", "plan_dispatch_ws", "plan_layout_dispatch", "plan_combine",
+    "plan_layout_ws", "plan_dispatch_planned",
     "MOE_PLAN_BYTES",
 ]

@@ -220,10 +220,118 @@ int run_combine(const CombineArgs &a, hipStream_t stream) {
                                         a.slot_idx, a.topk_weights, a.S, a.H, a.K, a.y, stream));
 }
 
+// The workspace of moe_layout_ws / moe_dispatch_planned / moe_layout_dispatch_ws: the pack plan
+// first (its size depends on S, K, C and quant only, so the dispatch can find it without E), then the
+// layout's scratch. Byte offsets; every part 256-aligned.
+struct LayoutWsShape {
+    int64_t plan_bytes, colexcl, bucket, chan, total;
+    int planned;   // 0: token-order pack; 1: plan written by the layout; 2: separate plan kernel
+    moe::PackChunks chunks;
+};
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+LayoutWsShape plan_part(int32_t S, int32_t K, int32_t C, int32_t quant) {
+    LayoutWsShape w{};
+    if (moe::pack_planned_used(S, K, quant)) {
+        if (moe::channel_chunks(S, K, C, &w.chunks)) {
+            w.planned = 1;
+            w.plan_bytes = moe::chunk_plan_bytes(w.chunks);
+        } else {
+            w.planned = 2;
+            w.plan_bytes = moe::pack_plan_bytes(S, K);
+        }
+    }
+    w.total = w.plan_bytes;
+    return w;
+}
+
+LayoutWsShape layout_ws_shape(int32_t S, int32_t K, int32_t E, int32_t C, int32_t quant) {
+    LayoutWsShape w = plan_part(S, K, C, quant);
+    w.colexcl = align256(w.plan_bytes);
+    w.bucket = w.colexcl + align256((int64_t)E * C * 4);
+    w.chan = w.bucket + align256((int64_t)S * K * 4);
+    w.total = w.chan + (int64_t)2 * C * 4;
+    return w;
+}
+
+// Checks of moe_layout_ws on top of check_layout (sets a.form): quant and, for the two-launch form,
+// the workspace.
+int check_layout_ws(LayoutArgs &a, int32_t path, int32_t quant, const void *workspace,
+                    int64_t workspace_bytes) {
+    int st = check_layout(a, path);
+    if (st != MOE_OK) return st;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    if (a.form == 1) return MOE_OK;
+    if (!workspace) return MOE_ERR_ARG;
+    if (!aligned(workspace, 16)) return MOE_ERR_ALIGN;
+    if (workspace_bytes < layout_ws_shape(a.S, a.K, a.E, a.C, quant).total) return MOE_ERR_WINDOW;
+    return MOE_OK;
+}
+
+int run_layout_ws(const LayoutArgs &a, int32_t quant, void *workspace, hipStream_t stream) {
+    if (a.form == 1) return run_layout(a, stream);
+    const LayoutWsShape w = layout_ws_shape(a.S, a.K, a.E, a.C, quant);
+    uint8_t *base = static_cast<uint8_t *>(workspace);
+    const moe::LayoutWorkspace lw{reinterpret_cast<int32_t *>(base + w.colexcl),
+                                  reinterpret_cast<int32_t *>(base + w.bucket),
+                                  reinterpret_cast<int32_t *>(base + w.chan),
+                                  w.planned == 1 ? reinterpret_cast<int2 *>(base) : nullptr, w.chunks};
+    return from_hip(moe::launch_layout_ws(a.topk_idx, a.S, a.K, a.E, a.P, a.C, a.is_token_in_rank,
+                                          a.num_tokens_per_rank, a.num_tokens_per_expert,
+                                          a.rank_prefix_matrix, a.expert_prefix_matrix,
+                                          a.rank_slot_base, a.expert_slot_base, a.slot_idx,
+                                          a.status, lw, stream));
+}
+
+int check_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                           int32_t C, int32_t quant, const void *window, int64_t window_bytes,
+                           const void *workspace, int64_t workspace_bytes) {
+    const int st = moe::check_dispatch(x, slot_idx, S, H, K, quant, window, window_bytes);
+    if (st != MOE_OK) return st;
+    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    const LayoutWsShape w = plan_part(S, K, C, quant);
+    if (w.planned == 0) return MOE_OK;
+    if (!workspace) return MOE_ERR_ARG;
+    if (!aligned(workspace, 16)) return MOE_ERR_ALIGN;
+    if (workspace_bytes < w.plan_bytes) return MOE_ERR_WINDOW;
+    return MOE_OK;
+}
+
+int run_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                         int32_t C, int32_t quant, int32_t src_rank, void *window, void *workspace,
+                         hipStream_t stream) {
+    const LayoutWsShape w = plan_part(S, K, C, quant);
+    if (w.planned == 1)
+        return from_hip(moe::launch_pack_from_plan(x, workspace, w.chunks, S, H, K, src_rank, window,
+                                                   stream));
+    if (w.planned == 2)
+        return from_hip(moe::launch_pack_planned(x, slot_idx, S, H, K, src_rank, window, workspace,
+                                                 stream));
+    return from_hip(moe::launch_pack(x, slot_idx, S, H, K, quant, src_rank, window, stream));
+}
+
+struct LayoutWsArgs {
+    LayoutArgs layout;
+    int32_t quant;
+    void *workspace;
+};
+
+struct DispatchPlannedArgs {
+    const void *x;
+    const int32_t *slot_idx;
+    int32_t S, H, K, C, quant, src_rank;
+    void *window;
+    void *workspace;
+};
+
 // What a moe_plan holds: a tag, the call kind and its checked arguments.
 struct PlanRecord {
     static constexpr uint64_t kMagic = 0x6d6f65706c616e31ull;  // "moeplan1"
-    enum Kind : int32_t { kNone = 0, kLayout = 1, kDispatch = 2, kLayoutDispatch = 3, kCombine = 4 };
+    enum Kind : int32_t {
+        kNone = 0, kLayout = 1, kDispatch = 2, kLayoutDispatch = 3, kCombine = 4, kLayoutWs = 5,
+        kDispatchPlanned = 6
+    };
     uint64_t magic;
     Kind kind;
     union {
@@ -231,6 +339,8 @@ struct PlanRecord {
         DispatchArgs dispatch;
         LayoutDispatchArgs layout_dispatch;
         CombineArgs combine;
+        LayoutWsArgs layout_ws;
+        DispatchPlannedArgs dispatch_planned;
     };
 };
 static_assert(sizeof(PlanRecord) <= sizeof(moe_plan), "moe_plan is too small for a plan record");
@@ -360,6 +470,67 @@ int moe_layout_dispatch(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E
                                   src_rank, window, window_bytes, MOE_LAYOUT_AUTO, stream);
 }
 
+int64_t moe_layout_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                                             int32_t quant, int32_t path) {
+    int st = check_tokens(S, K);
+    if (st != MOE_OK) return st;
+    st = check_experts(E, P);
+    if (st != MOE_OK) return st;
+    if (C < 1 || C > S || C > MOE_MAX_CHANNELS) return MOE_ERR_ARG;
+    if (!moe::valid_quant(quant)) return MOE_ERR_ARG;
+    const int form = pick_layout(path, S, K, E, P, C);
+    if (form < 0) return MOE_ERR_ARG;
+    if (form == 2) return MOE_ERR_UNSUPPORTED;
+    return form == 1 ? 0 : layout_ws_shape(S, K, E, C, quant).total;
+}
+
+int moe_layout_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                  uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                  int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                  int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
+                  int32_t *slot_idx, int32_t *status, int32_t quant, int32_t path, void *workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
+    LayoutArgs a{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                 num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix, rank_slot_base,
+                 expert_slot_base, slot_idx, status, 0};
+    const int st = check_layout_ws(a, path, quant, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    return run_layout_ws(a, quant, workspace, stream);
+}
+
+int moe_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                         int32_t C, int32_t quant, int32_t src_rank, void *window,
+                         int64_t window_bytes, const void *workspace, int64_t workspace_bytes,
+                         hipStream_t stream) {
+    const int st = check_dispatch_planned(x, slot_idx, S, H, K, C, quant, window, window_bytes,
+                                          workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    return run_dispatch_planned(x, slot_idx, S, H, K, C, quant, src_rank, window,
+                                const_cast<void *>(workspace), stream);
+}
+
+int moe_layout_dispatch_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                           int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                           int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                           int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                           int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                           const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                           int64_t window_bytes, int32_t path, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream) {
+    LayoutDispatchArgs a{{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                          num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                          rank_slot_base, expert_slot_base, slot_idx, status, 0},
+                         x, H, quant, src_rank, window};
+    int st = check_layout_dispatch(a, path, window_bytes);
+    if (st != MOE_OK) return st;
+    if (a.layout.form == 1) return run_layout_dispatch(a, stream);  // one kernel, no workspace
+    st = check_layout_ws(a.layout, path, quant, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    st = run_layout_ws(a.layout, quant, workspace, stream);
+    if (st != MOE_OK) return st;
+    return run_dispatch_planned(x, slot_idx, S, H, K, C, quant, src_rank, window, workspace, stream);
+}
+
 int moe_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                 const int32_t *slot_idx, const float *topk_weights, int32_t S, int32_t H,
                 int32_t K, void *y, hipStream_t stream) {
@@ -423,6 +594,37 @@ int moe_plan_combine(moe_plan *plan, const void *expert_out, int64_t row_stride_
     return store_plan(plan, rec, check_combine(rec.combine));
 }
 
+int moe_plan_layout_ws(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K, int32_t E,
+                       int32_t P, int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                       int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                       int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                       int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t quant,
+                       int32_t path, void *workspace, int64_t workspace_bytes) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kLayoutWs;
+    rec.layout_ws = LayoutWsArgs{{topk_idx, S, K, E, P, C, is_token_in_rank, num_tokens_per_rank,
+                                  num_tokens_per_expert, rank_prefix_matrix, expert_prefix_matrix,
+                                  rank_slot_base, expert_slot_base, slot_idx, status, 0},
+                                 quant, workspace};
+    return store_plan(plan, rec,
+                      check_layout_ws(rec.layout_ws.layout, path, quant, workspace, workspace_bytes));
+}
+
+int moe_plan_dispatch_planned(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
+                              int32_t H, int32_t K, int32_t C, int32_t quant, int32_t src_rank,
+                              void *window, int64_t window_bytes, const void *workspace,
+                              int64_t workspace_bytes) {
+    if (!plan) return MOE_ERR_ARG;
+    PlanRecord rec{};
+    rec.kind = PlanRecord::kDispatchPlanned;
+    rec.dispatch_planned = DispatchPlannedArgs{x, slot_idx, S, H, K, C, quant, src_rank, window,
+                                               const_cast<void *>(workspace)};
+    return store_plan(plan, rec,
+                      check_dispatch_planned(x, slot_idx, S, H, K, C, quant, window, window_bytes,
+                                             workspace, workspace_bytes));
+}
+
 int moe_plan_run(const moe_plan *plan, hipStream_t stream) {
     if (!plan) return MOE_ERR_ARG;
     PlanRecord rec;
@@ -433,6 +635,14 @@ int moe_plan_run(const moe_plan *plan, hipStream_t stream) {
         case PlanRecord::kDispatch: return run_dispatch_ws(rec.dispatch, stream);
         case PlanRecord::kLayoutDispatch: return run_layout_dispatch(rec.layout_dispatch, stream);
         case PlanRecord::kCombine: return run_combine(rec.combine, stream);
+        case PlanRecord::kLayoutWs:
+            return run_layout_ws(rec.layout_ws.layout, rec.layout_ws.quant, rec.layout_ws.workspace,
+                                 stream);
+        case PlanRecord::kDispatchPlanned: {
+            const DispatchPlannedArgs &d = rec.dispatch_planned;
+            return run_dispatch_planned(d.x, d.slot_idx, d.S, d.H, d.K, d.C, d.quant, d.src_rank,
+                                        d.window, d.workspace, stream);
+        }
         default: return MOE_ERR_ARG;
     }
 }

@@ -135,6 +135,59 @@ hipError_t launch_pack_planned(const void *x, const int32_t *slot_idx, int32_t S
                                int32_t K, int32_t src_rank, void *window, void *workspace,
                                hipStream_t stream);
 
+// How the planned pack's record lists map to tokens: group g covers tokens
+// [g*a + min(g*d, b), (g+1)*a + min((g+1)*d, b)) and belongs to XCD g % 8, whose list holds nsx
+// groups of cap records; every group has at most 2^lt tokens. Token chunks of the plan kernel are
+// (a, d, b) = (Tc, 0, 0); groups of cpc channels of the layout are (cpc*(S/C), cpc, S%C).
+struct PackChunks {
+    int lt, nsub, nsx, cap, a, d, b, cpc;
+};
+
+inline PackChunks token_chunks(int32_t S, int32_t K) {
+    const PlanShape p = plan_shape(S, K);
+    return PackChunks{p.lt, p.nsub, p.nsx, K << p.lt, 1 << p.lt, 0, 0, 0};
+}
+
+// Groups of whole channels for a plan written by the layout itself: possible when a channel holds
+// at most 1024 entries (ceil(S/C) * K <= 1024); cpc = 1024 / (ceil(S/C) * K) channels per group.
+inline bool channel_chunks(int32_t S, int32_t K, int32_t C, PackChunks *pc) {
+    const int per = S / C, rem = S % C;
+    const int maxchan = per + (rem > 0 ? 1 : 0);
+    if ((int64_t)maxchan * K > 1024) return false;
+    const int cpc = 1024 / (maxchan * K);
+    const int ngroups = (C + cpc - 1) / cpc;
+    int lt = 0;
+    while ((1 << lt) < cpc * maxchan) ++lt;
+    *pc = PackChunks{lt, ngroups, (ngroups + 7) / 8, 1024, cpc * per, cpc, rem, cpc};
+    return true;
+}
+
+inline int64_t chunk_plan_bytes(const PackChunks &pc) { return (int64_t)8 * pc.nsx * pc.cap * 8; }
+
+// The planned pack kernel alone, from record lists already in `plan` laid out by `pc`.
+hipError_t launch_pack_from_plan(const void *x, const void *plan, const PackChunks &pc, int32_t S,
+                                 int32_t H, int32_t K, int32_t src_rank, void *window,
+                                 hipStream_t stream);
+
+// Scratch of the two-launch layout (moe_layout_dispatch_ws): colexcl int32 [E, C], bucket int32
+// [S*K], chan int32 [2C], and, when plan is not null, the pack plan laid out by chunks.
+struct LayoutWorkspace {
+    int32_t *colexcl;
+    int32_t *bucket;
+    int32_t *chan;
+    int2 *plan;
+    PackChunks chunks;
+};
+
+// Count kernel (workspace form) + finalize kernel: the outputs of launch_layout, and the pack plan
+// when ws.plan is set (ws.chunks from channel_chunks).
+hipError_t launch_layout_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                            int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                            int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                            int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                            int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                            const LayoutWorkspace &ws, hipStream_t stream);
+
 hipError_t launch_combine(const void *expert_out, int64_t row_stride_bytes, int64_t expert_rows,
                           const int32_t *slot_idx, const float *topk_weights, int32_t S,
                           int32_t H, int32_t K, void *y, hipStream_t stream);

@@ -18,6 +18,9 @@
 //         rows into its L2 and the memory-side cache, then stores its records in slot order:
 //         consecutive workgroups write neighbouring slots, and the K re-reads of a row hit cache.
 //
+// moe_layout_ws can write the record lists itself (groups of whole channels instead of token chunks;
+// the PackChunks argument says which), and the pack kernel then runs alone (moe_dispatch_planned).
+//
 // Measured at S=4096, H=7168, K=8 with x in HBM: 82 us for the pack kernel and 3.4 us for the plan,
 // against 100 us for the token-order pack; at S=8192, P=128 with Zipf routing 173 + 3.6 us against
 // 194 us. The pack kernel's prologue holds no runtime integer division (a 32-bit multiply-high
@@ -92,26 +95,28 @@ __global__ __launch_bounds__(kPlanThreads) void pack_plan_kernel(const int32_t *
     if (tid >= total && tid < TcK) out[tid] = int2{-1, 0};
 }
 
-// grid = 8 * (nsx * Tc + nsx * Tc * K * nparts) workgroups of kPartLanes. Workgroup b: XCD
-// x = b % 8, index m = b / 8 in that XCD's sequence: m < nsx * Tc reads row (8(m >> lt) + x) << lt
-// + (m & (Tc - 1)) and stores nothing; otherwise record (m - nsx * Tc) / nparts of list x, part
-// (m - nsx * Tc) % nparts (the quotient by a multiply-high with np_magic = ceil(2^32 / nparts),
+// grid = 8 * (nsx * 2^lt + nsx * cap * nparts) workgroups of kPartLanes. Workgroup b: XCD
+// x = b % 8, index m = b / 8 in that XCD's sequence: m < nsx * 2^lt reads token m & (2^lt - 1) of
+// group 8(m >> lt) + x (if the group has that many) and stores nothing; otherwise record
+// (m - nsx * 2^lt) / nparts of list x, part (m - nsx * 2^lt) % nparts (the quotient by a multiply-high with np_magic = ceil(2^32 / nparts),
 // exact for nparts in [2, 32] and indices below 2^24; nparts = 1 needs no division and its
 // magic, 2^32, would not fit in 32 bits).
 __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const uint8_t *__restrict__ x, const int2 *__restrict__ plan, int S, int K, int nvec,
-    int nparts, uint32_t np_magic, int lt, int nsx, int nsub, SlotGeom g, int src_rank,
+    int nparts, uint32_t np_magic, PackChunks pc, SlotGeom g, int src_rank,
     uint8_t *__restrict__ window) {
     const int b = blockIdx.x;
     const int xcd = b & 7;
     const int m = b >> 3;
-    const int npf = nsx << lt;
+    const int npf = pc.nsx << pc.lt;
     const int lane = threadIdx.x;
     const int row_bytes = nvec << 4;
     if (m < npf) {
-        const int c = ((m >> lt) << 3) + xcd;
-        const int t = (c << lt) + (m & ((1 << lt) - 1));
-        if (c >= nsub || t >= S) return;
+        const int c = ((m >> pc.lt) << 3) + xcd;  // group
+        const int tc0 = c * pc.a + min(c * pc.d, pc.b);
+        const int tc1 = (c + 1) * pc.a + min((c + 1) * pc.d, pc.b);
+        const int t = tc0 + (m & ((1 << pc.lt) - 1));
+        if (c >= pc.nsub || t >= tc1 || t >= S) return;
         const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
         uint32_t acc = 0;
         for (int q = 0; q < nparts; ++q) acc ^= load16(src, (q * kPartLanes + lane) << 4).x;
@@ -121,10 +126,11 @@ __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const uint32_t mp = (uint32_t)(m - npf);
     const uint32_t item = nparts == 1 ? mp : __umulhi(mp, np_magic);
     const int q = (int)(mp - item * (uint32_t)nparts);
-    const int2 e = plan[(int64_t)xcd * nsx * (K << lt) + item];
+    const int2 e = plan[(int64_t)xcd * pc.nsx * pc.cap + item];
     const int64_t s = e.x;
     if (s < 0 || s >= (int64_t)S * K) return;
     const int t = e.y >> 4, k = e.y & 15;
+    if ((unsigned)t >= (unsigned)S || k >= K) return;  // a record of another table: never outside x
     const int v = q * kPartLanes + lane;
     const u32x4 val = load16(rsrc(x + (int64_t)t * row_bytes, row_bytes), v << 4);
     const __amdgpu_buffer_rsrc_t dst = rsrc(window + s * g.slot_bytes, g.tail_end);
@@ -135,25 +141,30 @@ __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
 
 }  // namespace
 
+hipError_t launch_pack_from_plan(const void *x, const void *plan, const PackChunks &pc, int32_t S,
+                                 int32_t H, int32_t K, int32_t src_rank, void *window,
+                                 hipStream_t stream) {
+    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
+    const int nvec = H / 8;
+    const int nparts = (nvec + kPartLanes - 1) / kPartLanes;
+    const uint32_t magic = nparts > 1 ? (uint32_t)((0x100000000ull + nparts - 1) / nparts) : 0u;
+    const int64_t nwg = 8 * (((int64_t)pc.nsx << pc.lt) + (int64_t)pc.nsx * pc.cap * nparts);
+    hipLaunchKernelGGL(pack_planned_kernel, dim3((uint32_t)nwg), dim3(kPartLanes), 0, stream,
+                       static_cast<const uint8_t *>(x), static_cast<const int2 *>(plan), S, K, nvec,
+                       nparts, magic, pc, g, src_rank, static_cast<uint8_t *>(window));
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H,
                                int32_t K, int32_t src_rank, void *window, void *workspace,
                                hipStream_t stream) {
-    const SlotGeom g = slot_geom(H, MOE_QUANT_NONE);
     const PlanShape p = plan_shape(S, K);
     int2 *plan = static_cast<int2 *>(workspace);
     hipLaunchKernelGGL(pack_plan_kernel, dim3(8 * p.nsx), dim3(kPlanThreads), 0, stream, slot_idx, S,
                        K, p.lt, p.nsx, p.shift, plan);
-    hipError_t err = hipGetLastError();
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int nvec = H / 8;
-    const int nparts = (nvec + kPartLanes - 1) / kPartLanes;
-    const uint32_t magic = nparts > 1 ? (uint32_t)((0x100000000ull + nparts - 1) / nparts) : 0u;
-    const int64_t Tc = int64_t(1) << p.lt;
-    const int64_t nwg = 8 * ((int64_t)p.nsx * Tc + (int64_t)p.nsx * Tc * K * nparts);
-    hipLaunchKernelGGL(pack_planned_kernel, dim3((uint32_t)nwg), dim3(kPartLanes), 0, stream,
-                       static_cast<const uint8_t *>(x), plan, S, K, nvec, nparts, magic, p.lt, p.nsx,
-                       p.nsub, g, src_rank, static_cast<uint8_t *>(window));
-    return hipGetLastError();
+    return launch_pack_from_plan(x, plan, token_chunks(S, K), S, H, K, src_rank, window, stream);
 }
 
 }  // namespace moe

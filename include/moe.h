@@ -237,6 +237,62 @@ int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_
                            const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
                            int64_t window_bytes, int32_t path, hipStream_t stream);
 
+/* The layout and the pack with a caller workspace: the outputs of moe_layout_ex and the window bytes
+ * of moe_dispatch, in fewer launches. For tables that do not take the single kernel, the layout runs
+ * as two kernels instead of three: a count kernel per channel that also groups each channel's
+ * entries by expert into the workspace, then workgroups per expert that scan its prefix row and hand
+ * its entries their slots straight from those groups (the per-expert offset + running count of
+ * "HCCL Window 模式 (Non-SHMEM) 代码深度剖析", section 3.6, with the counts of "Ascend DeepEP MoE
+ * Dispatch Optimization", section "Notify 先交换数量和前缀"). In bf16 mode with at least 8192 entries
+ * and at most 1024 entries a channel (ceil(S / C) * K <= 1024), that second kernel also writes the
+ * plan of the planned pack (see moe_dispatch_ws), so no separate plan kernel runs.
+ *
+ * The workspace (device memory, 16-byte aligned, contents overwritten) holds the pack plan first,
+ * then the layout's scratch; calls that may run at the same time need workspaces of their own.
+ *
+ * moe_layout_dispatch_workspace_bytes(S, K, E, P, C, quant, path): the bytes these calls need for
+ *      these arguments: 0 when the layout takes the single kernel (its table is small, see
+ *      moe_layout_ex); negative moe_status on bad arguments (those of moe_layout_ex, quant).
+ * moe_layout_ws: moe_layout_ex's arguments plus quant (the payload type the following
+ *      moe_dispatch_planned will use: the plan is written only for MOE_QUANT_NONE) and the workspace
+ *      (NULL allowed when the size above is 0; MOE_ERR_ARG if NULL otherwise, MOE_ERR_ALIGN if not
+ *      16-byte aligned, MOE_ERR_WINDOW if workspace_bytes is below that size). Enqueues 1 kernel
+ *      (single form) or 2.
+ * moe_dispatch_planned: the window bytes of moe_dispatch for slot_idx (the one moe_layout_ws wrote),
+ *      using the plan moe_layout_ws left in the same workspace; S, K, C and quant must be those of
+ *      that moe_layout_ws call, and the workspace must not have been written in between (a plan from
+ *      another table writes that table's bytes; records are bounds-checked, so never outside the
+ *      window or x). Where the layout writes no plan, the call runs moe_dispatch_ws's plan kernel on
+ *      slot_idx (bf16, S*K >= 8192) or the token-order pack (no workspace needed). Checks: those of
+ *      moe_dispatch, C in [1, min(S, MOE_MAX_CHANNELS)], then the workspace as above, against the plan's
+ *      part only. Enqueues 1 kernel (2 when it runs the plan kernel).
+ * moe_layout_dispatch_ws: moe_layout_dispatch_ex's arguments plus the workspace: moe_layout_ws then
+ *      moe_dispatch_planned (the single layout + pack kernel of moe_layout_dispatch for small tables).
+ */
+int64_t moe_layout_dispatch_workspace_bytes(int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                                             int32_t quant, int32_t path);
+
+int moe_layout_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P, int32_t C,
+                  uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                  int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                  int32_t *expert_prefix_matrix, int32_t *rank_slot_base, int32_t *expert_slot_base,
+                  int32_t *slot_idx, int32_t *status, int32_t quant, int32_t path, void *workspace,
+                  int64_t workspace_bytes, hipStream_t stream);
+
+int moe_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
+                         int32_t C, int32_t quant, int32_t src_rank, void *window,
+                         int64_t window_bytes, const void *workspace, int64_t workspace_bytes,
+                         hipStream_t stream);
+
+int moe_layout_dispatch_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
+                           int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                           int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                           int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                           int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status,
+                           const void *x, int32_t H, int32_t quant, int32_t src_rank, void *window,
+                           int64_t window_bytes, int32_t path, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+
 /* Combine: y[t] = bf16( sum over k = 0..K-1 ascending with slot_idx[t, k] valid of
  *                       fp32(topk_weights[t, k] * fp32(expert_out row slot_idx[t, k])) ),
  * accumulated in fp32 from +0.0, each product and each sum rounded to fp32 (no fused
@@ -407,7 +463,9 @@ int moe_unpack_padded(const void *window, int64_t window_bytes, const int32_t *e
  *   moe_plan_layout           -> moe_layout_ex (path as there)
  *   moe_plan_dispatch_ws      -> moe_dispatch_ws
  *   moe_plan_layout_dispatch  -> moe_layout_dispatch_ex (path as there)
- *   moe_plan_combine          -> moe_combine */
+ *   moe_plan_combine          -> moe_combine
+ *   moe_plan_layout_ws        -> moe_layout_ws (path as there)
+ *   moe_plan_dispatch_planned -> moe_dispatch_planned */
 typedef struct {
     uint64_t opaque[40];
 } moe_plan;
@@ -434,6 +492,16 @@ int moe_plan_combine(moe_plan *plan, const void *expert_out, int64_t row_stride_
                      int64_t expert_rows, const int32_t *slot_idx, const float *topk_weights,
                      int32_t S, int32_t H, int32_t K, void *y);
 
+int moe_plan_layout_ws(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32_t K, int32_t E,
+                       int32_t P, int32_t C, uint8_t *is_token_in_rank, int32_t *num_tokens_per_rank,
+                       int32_t *num_tokens_per_expert, int32_t *rank_prefix_matrix,
+                       int32_t *expert_prefix_matrix, int32_t *rank_slot_base,
+                       int32_t *expert_slot_base, int32_t *slot_idx, int32_t *status, int32_t quant,
+                       int32_t path, void *workspace, int64_t workspace_bytes);
+int moe_plan_dispatch_planned(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
+                              int32_t H, int32_t K, int32_t C, int32_t quant, int32_t src_rank,
+                              void *window, int64_t window_bytes, const void *workspace,
+                              int64_t workspace_bytes);
 int moe_plan_run(const moe_plan *plan, hipStream_t stream);
 
 /* Static description of a moe_status value (never NULL). */

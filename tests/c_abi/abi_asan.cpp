@@ -202,6 +202,79 @@ int main() {
                    only(stubs::kPack, 1),
                "dispatch_ws fp8 -> token-order quantised pack, no workspace needed");
     }
+    {
+        // moe_layout_dispatch_ws: every part of the workspace inside it, 256-byte aligned, apart and
+        // as large as its kernel writes; the plan first, where moe_dispatch_planned finds it.
+        struct Case {
+            int S, K, E, P, C, quant;
+            stubs::Launcher launcher;
+            const char *what;
+        };
+        const Case cases[] = {
+            {4096, 8, 256, 8, 128, 0, stubs::kPackFromPlan, "layout_dispatch_ws bf16, 256 entries a channel -> plan by the layout"},
+            {8192, 8, 256, 128, 128, 0, stubs::kPackFromPlan, "layout_dispatch_ws bf16, 512 entries a channel"},
+            {4096, 8, 256, 8, 16, 0, stubs::kPackPlanned, "layout_dispatch_ws bf16, 2048 entries a channel -> plan kernel"},
+            {4096, 8, 256, 8, 1, 0, stubs::kPackPlanned, "layout_dispatch_ws bf16, one channel"},
+            {65536, 16, 512, 256, 4096, 0, stubs::kPackFromPlan, "layout_dispatch_ws at the maxima"},
+            {65536, 16, 384, 384, 1, 0, stubs::kPackPlanned, "layout_dispatch_ws at the maxima, one channel"},
+            {4096, 8, 256, 8, 128, 1, stubs::kPack, "layout_dispatch_ws fp8 -> token-order pack"},
+            {1000, 8, 64, 8, 128, 0, stubs::kPack, "layout_dispatch_ws bf16 below 8192 entries -> token-order pack"},
+        };
+        for (const Case &c : cases) {
+            const int64_t wsb = moe_layout_dispatch_workspace_bytes(c.S, c.K, c.E, c.P, c.C, c.quant, 0);
+            const int64_t wb = moe_window_bytes(c.S, c.K, 64);
+            const uintptr_t ws = 0x40000000;
+            void *wsp = reinterpret_cast<void *>(ws);
+            stubs::reset();
+            const int st = moe_layout_dispatch_ws(I, c.S, c.K, c.E, c.P, c.C, U, I, I, I, I, I, I, I, I, A, 64,
+                                                  c.quant, 0, A, wb, MOE_LAYOUT_AUTO, wsp, wsb, nullptr);
+            bool ok = st == MOE_OK && only(stubs::kLayoutWs, 1, c.launcher, 1);
+            const moe::LayoutWorkspace w = stubs::last_ws;
+            const void *plan = stubs::last_plan;
+            const moe::PackChunks pc = stubs::last_chunks;
+            auto at = [&](const void *p) { return (int64_t)(reinterpret_cast<uintptr_t>(p) - ws); };
+            const int64_t o_col = at(w.colexcl), o_bucket = at(w.bucket), o_chan = at(w.chan);
+            int64_t plan_end = 0;
+            if (c.launcher == stubs::kPackFromPlan) {
+                plan_end = 64LL * pc.nsx * pc.cap;
+                ok = ok && w.plan != nullptr && at(w.plan) == 0 && plan == w.plan && 8LL * pc.nsx >= pc.nsub &&
+                     (int64_t)pc.cpc * ((c.S + c.C - 1) / c.C) * c.K <= pc.cap &&
+                     (1 << pc.lt) >= pc.cpc * ((c.S + c.C - 1) / c.C);
+            } else if (c.launcher == stubs::kPackPlanned) {
+                plan_end = moe_dispatch_workspace_bytes(c.S, c.K, 0);
+                ok = ok && w.plan == nullptr && at(plan) == 0;
+            } else {
+                ok = ok && w.plan == nullptr;
+            }
+            ok = ok && o_col >= plan_end && o_col % 256 == 0 && o_bucket >= o_col + (int64_t)c.E * c.C * 4 &&
+                 o_bucket % 256 == 0 && o_chan >= o_bucket + (int64_t)c.S * c.K * 4 && o_chan % 256 == 0 &&
+                 o_chan + 2LL * c.C * 4 <= wsb;
+            expect(ok, c.what);
+            expect(moe_layout_dispatch_ws(I, c.S, c.K, c.E, c.P, c.C, U, I, I, I, I, I, I, I, I, A, 64, c.quant, 0, A,
+                                          wb, MOE_LAYOUT_AUTO, wsp, wsb - 1, nullptr) == MOE_ERR_WINDOW,
+                   "layout_dispatch_ws one workspace byte short");
+            // the same work as two calls: the layout, then the pack from the plan it left
+            stubs::reset();
+            ok = moe_layout_ws(I, c.S, c.K, c.E, c.P, c.C, U, I, I, I, I, I, I, I, I, c.quant, 0, wsp, wsb, nullptr) ==
+                     MOE_OK &&
+                 only(stubs::kLayoutWs, 1) && (stubs::last_ws.plan == nullptr) == (c.launcher != stubs::kPackFromPlan);
+            expect(ok, "layout_ws alone");
+            stubs::reset();
+            ok = moe_dispatch_planned(A, I, c.S, 64, c.K, c.C, c.quant, 0, A, wb, wsp, plan_end, nullptr) == MOE_OK &&
+                 only(c.launcher, 1) && (c.launcher == stubs::kPack || stubs::last_plan == wsp);
+            expect(ok, "dispatch_planned with exactly the plan's bytes");
+            if (plan_end > 0)
+                expect(moe_dispatch_planned(A, I, c.S, 64, c.K, c.C, c.quant, 0, A, wb, wsp, plan_end - 1, nullptr) ==
+                           MOE_ERR_WINDOW,
+                       "dispatch_planned one plan byte short");
+        }
+        stubs::reset();
+        expect(moe_layout_dispatch_workspace_bytes(64, 8, 256, 8, 16, 0, MOE_LAYOUT_AUTO) == 0 &&
+                   moe_layout_dispatch_ws(I, 64, 8, 256, 8, 16, U, I, I, I, I, I, I, I, I, A, 7168, 0, 0, A, win,
+                                          MOE_LAYOUT_AUTO, nullptr, 0, nullptr) == MOE_OK &&
+                   only(stubs::kLayoutDispatchSmall, 1),
+               "layout_dispatch_ws on a small table -> one kernel, no workspace");
+    }
     stubs::reset();
     expect(moe_combine(A, 14848, 512, I, F, 64, 7168, 8, A, nullptr) == MOE_OK && only(stubs::kCombine, 1),
            "combine -> launch_combine");

@@ -5,8 +5,14 @@
 
 namespace stubs {
 int calls[kLaunchers];
+moe::LayoutWorkspace last_ws;
+const void *last_plan;
+moe::PackChunks last_chunks;
 void reset() {
     for (int &c : calls) c = 0;
+    last_ws = moe::LayoutWorkspace{};
+    last_plan = nullptr;
+    last_chunks = moe::PackChunks{};
 }
 }  // namespace stubs
 
@@ -17,6 +23,20 @@ hipError_t launch_layout(const int32_t *, int32_t, int32_t, int32_t, int32_t, in
                          int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *,
                          hipStream_t) {
     ++calls[stubs::kLayout];
+    return hipSuccess;
+}
+hipError_t launch_layout_ws(const int32_t *, int32_t, int32_t, int32_t, int32_t, int32_t, uint8_t *, int32_t *,
+                            int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *,
+                            const LayoutWorkspace &ws, hipStream_t) {
+    ++calls[stubs::kLayoutWs];
+    stubs::last_ws = ws;
+    return hipSuccess;
+}
+hipError_t launch_pack_from_plan(const void *, const void *plan, const PackChunks &pc, int32_t, int32_t, int32_t,
+                                 int32_t, void *, hipStream_t) {
+    ++calls[stubs::kPackFromPlan];
+    stubs::last_plan = plan;
+    stubs::last_chunks = pc;
     return hipSuccess;
 }
 hipError_t launch_layout_small(const int32_t *, int32_t, int32_t, int32_t, int32_t, int32_t, uint8_t *,
@@ -53,9 +73,10 @@ hipError_t launch_pack(const void *, const int32_t *, int32_t, int32_t, int32_t,
     ++calls[stubs::kPack];
     return hipSuccess;
 }
-hipError_t launch_pack_planned(const void *, const int32_t *, int32_t, int32_t, int32_t, int32_t, void *, void *,
-                               hipStream_t) {
+hipError_t launch_pack_planned(const void *, const int32_t *, int32_t, int32_t, int32_t, int32_t, void *,
+                               void *workspace, hipStream_t) {
     ++calls[stubs::kPackPlanned];
+    stubs::last_plan = workspace;
     return hipSuccess;
 }
 hipError_t launch_combine(const void *, int64_t, int64_t, const int32_t *, const float *, int32_t, int32_t,

@@ -214,6 +214,14 @@ def test_plans_check_like_the_calls_and_refuse_unfilled_plans():
     assert lib.moe_plan_combine(addr, A, 14000, 512, A, A, 64, 7168, 8, A) == moe.MOE_ERR_ARG
     assert lib.moe_plan_combine(addr, A, 14336, 512, A, A, 64, 7168, 8, A + 8) == moe.MOE_ERR_ALIGN
     assert lib.moe_plan_combine(None, A, 14336, 512, A, A, 64, 7168, 8, A) == moe.MOE_ERR_ARG
+    wsb = moe.moe_layout_dispatch_workspace_bytes(4096, 8, 256, 8, 128)
+    assert lib.moe_plan_layout_ws(addr, A, 4096, 8, 256, 8, 128, *outs, 0, 0, NULL, wsb) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_layout_ws(addr, A, 4096, 8, 256, 8, 128, *outs, 0, 0, A, wsb - 1) == moe.MOE_ERR_WINDOW
+    assert lib.moe_plan_layout_ws(addr, A, 4096, 8, 256, 8, 128, *outs, 4, 0, A, wsb) == moe.MOE_ERR_ARG
+    assert lib.moe_plan_dispatch_planned(addr, A, A, 4096, 7168, 8, 128, 0, 0, A, 4096 * 8 * 14848, A + 4,
+                                         wsb) == moe.MOE_ERR_ALIGN
+    assert lib.moe_plan_dispatch_planned(addr, A, A, 4096, 7168, 8, 0, 0, 0, A, 4096 * 8 * 14848, A,
+                                         wsb) == moe.MOE_ERR_ARG
     assert lib.moe_plan_run(addr, None) == moe.MOE_ERR_ARG
     assert buf.raw == bytes(moe.MOE_PLAN_BYTES)  # cleared after every failed check
 
@@ -416,6 +424,83 @@ def test_layout_dispatch_ex_validation():
                                       None) == moe.MOE_ERR_ARG
     assert lib.moe_layout_dispatch_ex(A, 64, 8, 256, 8, 16, *([A] * 9), A, 7168, 0, 0, A, 0,
                                       moe.MOE_LAYOUT_MULTI, None) == moe.MOE_ERR_WINDOW
+
+
+def test_layout_dispatch_workspace_bytes():
+    """0 for tables the single kernel takes; otherwise, each part rounded up to 256 bytes but the last:
+    the plan (in bf16 from 8192 entries on: 8 lists of ceil(groups / 8) groups of 1024 records when a
+    channel holds at most 1024 entries, else the plan kernel's size), colexcl [E, C], bucket [S*K],
+    chan [2C]."""
+    r = lambda v: (v + 255) // 256 * 256
+    f = moe.moe_layout_dispatch_workspace_bytes
+    assert f(64, 8, 256, 8, 16) == 0
+    assert f(64, 8, 256, 8, 16, path=moe.MOE_LAYOUT_MULTI) == r(256 * 16 * 4) + r(512 * 4) + 2 * 16 * 4
+    scratch = r(256 * 128 * 4) + r(4096 * 8 * 4) + 2 * 128 * 4
+    assert f(4096, 8, 256, 8, 128) == 8 * 4 * 1024 * 8 + scratch  # 4 channels a group, 32 groups
+    assert f(4096, 8, 256, 8, 128, moe.MOE_QUANT_FP8_E4M3_DYN) == scratch
+    scratch16 = r(256 * 16 * 4) + r(4096 * 8 * 4) + 2 * 16 * 4
+    assert f(4096, 8, 256, 8, 16) == moe.moe_dispatch_workspace_bytes(4096, 8) + scratch16
+    scratch_s = r(256 * 4096 * 4) + r(4096 * 8 * 4) + 2 * 4096 * 4
+    assert f(4096, 8, 256, 8, 4096) == 8 * 4 * 1024 * 8 + scratch_s  # 128 channels a group
+    lib = moe._lib
+    assert lib.moe_layout_dispatch_workspace_bytes(0, 8, 256, 8, 1, 0, 0) == moe.MOE_ERR_ARG
+    assert lib.moe_layout_dispatch_workspace_bytes(64, 8, 250, 8, 1, 0, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layout_dispatch_workspace_bytes(64, 8, 256, 8, 65, 0, 0) == moe.MOE_ERR_ARG
+    assert lib.moe_layout_dispatch_workspace_bytes(64, 8, 256, 8, 16, 3, 0) == moe.MOE_ERR_ARG
+    assert lib.moe_layout_dispatch_workspace_bytes(64, 8, 256, 8, 16, 0, 9) == moe.MOE_ERR_ARG
+    assert lib.moe_layout_dispatch_workspace_bytes(513, 8, 256, 8, 16, 0, 2) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_layout_dispatch_ws_validation():
+    """The checks of moe_layout_dispatch_ex, then the workspace: NULL, misaligned or short."""
+    lib = moe._lib
+    S, K, E, P, C, H = 4096, 8, 256, 8, 128, 7168
+    nb = S * K * 14848
+    wsb = moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C)
+
+    def call(ws=A, wsb=wsb, nbytes=nb, x=A, path=0, quant=0):
+        return lib.moe_layout_dispatch_ws(A, S, K, E, P, C, *([A] * 9), x, H, quant, 0, A, nbytes, path, ws, wsb,
+                                          None)
+
+    assert call(ws=NULL) == moe.MOE_ERR_ARG
+    assert call(ws=A + 8) == moe.MOE_ERR_ALIGN
+    assert call(wsb=wsb - 1) == moe.MOE_ERR_WINDOW
+    assert call(nbytes=nb - 1) == moe.MOE_ERR_WINDOW
+    assert call(x=NULL) == moe.MOE_ERR_ARG
+    assert call(x=A + 8) == moe.MOE_ERR_ALIGN
+    assert call(path=moe.MOE_LAYOUT_SINGLE) == moe.MOE_ERR_UNSUPPORTED
+    assert call(path=5) == moe.MOE_ERR_ARG
+    assert call(quant=4) == moe.MOE_ERR_ARG
+
+
+def test_layout_ws_and_dispatch_planned_validation():
+    lib = moe._lib
+    S, K, E, P, C, H = 4096, 8, 256, 8, 128, 7168
+    wsb = moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C)
+    plan = 8 * 4 * 1024 * 8
+
+    def layout(ws=A, nbytes=wsb, quant=0, path=0, S=S, C=C):
+        return lib.moe_layout_ws(A, S, K, E, P, C, *([A] * 9), quant, path, ws, nbytes, None)
+
+    assert layout(ws=NULL) == moe.MOE_ERR_ARG
+    assert layout(ws=A + 4) == moe.MOE_ERR_ALIGN
+    assert layout(nbytes=wsb - 1) == moe.MOE_ERR_WINDOW
+    assert layout(quant=3) == moe.MOE_ERR_ARG
+    assert layout(path=moe.MOE_LAYOUT_SINGLE) == moe.MOE_ERR_UNSUPPORTED
+    assert layout(C=0) == moe.MOE_ERR_ARG
+
+    def dispatch(ws=A, nbytes=plan, C=C, x=A, quant=0, win=S * K * 14848):
+        return lib.moe_dispatch_planned(x, A, S, H, K, C, quant, 0, A, win, ws, nbytes, None)
+
+    assert dispatch(ws=NULL) == moe.MOE_ERR_ARG
+    assert dispatch(ws=A + 8) == moe.MOE_ERR_ALIGN
+    assert dispatch(nbytes=plan - 1) == moe.MOE_ERR_WINDOW
+    assert dispatch(C=0) == moe.MOE_ERR_ARG
+    assert dispatch(C=S + 1) == moe.MOE_ERR_ARG
+    assert dispatch(C=4097) == moe.MOE_ERR_ARG
+    assert dispatch(x=NULL) == moe.MOE_ERR_ARG
+    assert dispatch(win=S * K * 14848 - 1) == moe.MOE_ERR_WINDOW
+    assert dispatch(quant=5) == moe.MOE_ERR_ARG
 
 
 def test_dedup_window_bytes():

@@ -534,6 +534,98 @@ def test_dispatch_ws_any_slot_table_and_reused_workspace(moe):
         ws.fill_(0xEE)
 
 
+# ---------------------------------------------------------------- layout + dispatch with a workspace
+
+
+def gpu_layout_dispatch_ws(moe, idx, x_bits, E, P, C, quant, src_rank=0, path=None, ws=None, ws_poison=0x5C,
+                           split=False):
+    """moe_layout_dispatch_ws, or (split) moe_layout_ws then moe_dispatch_planned on the same workspace."""
+    S, K = idx.shape
+    H = x_bits.shape[1]
+    path = 0 if path is None else path
+    win = torch.full((moe.moe_window_bytes(S, K, H),), POISON, dtype=torch.uint8, device=DEV)
+    if ws is None:
+        nws = moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C, quant, path)
+        ws = torch.full((nws,), ws_poison, dtype=torch.uint8, device=DEV) if nws else None
+    out = poisoned_layout(moe, S, K, E, P, C)
+    if split:
+        lay = moe.moe_layout_ws(to_dev(idx), E, P, C, ws, quant, out=out, path=path)
+        moe.moe_dispatch_planned(bf16_dev(x_bits), lay.slot_idx, win, ws, C, quant, src_rank)
+    else:
+        lay = moe.moe_layout_dispatch_ws(to_dev(idx), E, P, C, bf16_dev(x_bits), win, ws, quant, src_rank, out=out,
+                                         path=path)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in lay._asdict().items()}, win.cpu().numpy().reshape(S * K, -1)
+
+
+def check_layout_dispatch_ws(moe, idx, x_bits, E, P, C, quant, src_rank, what, path=None, ws=None, split=False):
+    got, win = gpu_layout_dispatch_ws(moe, idx, x_bits, E, P, C, quant, src_rank, path, ws, split=split)
+    ref = oracle.layout(idx, E, P, C)
+    assert_layout_equal(got, ref, what)
+    H = x_bits.shape[1]
+    assert_window_equal(win, oracle.dispatch_slots(x_bits, ref["slot_idx"], quant, src_rank),
+                        oracle.slot_geometry(H, quant), what)
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("cfg,quant", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 1), (5, 0), (5, 2)])
+def test_layout_dispatch_ws_workloads(moe, cfg, quant, layout_path, split):
+    """moe_layout_dispatch_ws (or moe_layout_ws + moe_dispatch_planned) on the workloads: the two-launch
+    layout writing the pack's plan at workloads 3 and 5 in bf16 (one batch per channel at 3, two at
+    5), the token-order pack in fp8 and int8."""
+    w = WORKLOADS[cfg]
+    inp = inputs(cfg)
+    note(f"layout_dispatch_ws cfg{cfg} quant {quant} path={layout_path} split={split}")
+    check_layout_dispatch_ws(moe, inp["topk_idx"], inp["x"], w.E, w.P, w.C, quant, 3,
+                             f"ws cfg{cfg} quant {quant}", layout_path, split=split)
+
+
+LAYOUT_DISPATCH_WS = [
+    # (S, K, H, E, P, C, quant, p_mask, p_bad, seed)
+    (4096, 8, 1024, 256, 8, 1, 0, 0.0, 0.0, 201),      # one channel of 32768 entries: plan kernel
+    (4096, 8, 1024, 256, 8, 16, 0, 0.05, 0.01, 202),   # 2048 entries per channel: plan kernel
+    (4096, 8, 1024, 256, 8, 32, 0, 0.05, 0.01, 203),   # 1024 entries per channel: one per group
+    (4096, 8, 1024, 256, 8, 4096, 0, 0.1, 0.0, 204),   # a token per channel: 128 channels a group
+    (3001, 3, 4112, 48, 4, 77, 0, 0.1, 0.02, 205),     # K = 3, ragged channels and row part
+    (600, 16, 7168, 128, 16, 40, 0, 0.2, 0.0, 206),    # K = 16: 15 tokens per channel
+    (2049, 8, 2048, 512, 128, 100, 0, 0.1, 0.05, 207),  # E at its maximum, bad ids (status 1)
+    (1536, 8, 256, 384, 384, 96, 0, 0.0, 0.0, 208),    # P at its maximum
+    (8192, 1, 2048, 16, 4, 8, 0, 0.1, 0.0, 209),       # K = 1, 1024 tokens per channel
+    (1700, 5, 16, 40, 8, 33, 0, 0.3, 0.05, 210),       # smallest H
+    (9000, 8, 64, 256, 8, 128, 0, 1.0, 0.0, 211),      # everything masked: nothing written
+    (1000, 8, 1024, 64, 8, 128, 0, 0.0, 0.0, 212),     # S*K = 8000: token-order pack, two launches
+    (2048, 8, 2048, 256, 8, 64, 2, 0.05, 0.01, 213),   # int8 codes
+    (65536, 2, 64, 64, 8, 4096, 0, 0.0, 0.0, 214),     # maximum S and C
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_DISPATCH_WS)
+def test_layout_dispatch_ws_shapes(moe, case):
+    """The two-launch layout at its edges: one channel (several batches; the separate plan kernel),
+    a token per channel, K in {1, 3, 5, 8, 16}, E and P at their maxima, bad and masked ids."""
+    S, K, H, E, P, C, quant, p_mask, p_bad, seed = case
+    rng = np.random.default_rng(seed)
+    idx = random_tiny_routing(rng, S, K, E, p_mask=p_mask, p_bad=p_bad)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    note(f"layout_dispatch_ws {case}")
+    check_layout_dispatch_ws(moe, idx, xb, E, P, C, quant, seed, str(case), path=1, split=seed % 2 == 0)
+
+
+def test_layout_dispatch_ws_reused_workspace(moe):
+    """Two tables through one workspace, the second after the workspace was overwritten, and the
+    first again: every output equal to the oracle's each time."""
+    rng = np.random.default_rng(215)
+    S, K, H, E, P, C = 2048, 8, 2048, 256, 8, 64
+    ws = torch.full((moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C),), 0x11, dtype=torch.uint8,
+                    device=DEV)
+    tables = [random_tiny_routing(rng, S, K, E, p_mask=0.1), random_tiny_routing(rng, S, K, E, p_mask=0.0)]
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    for rep, idx in enumerate(tables + tables[:1]):
+        note(f"layout_dispatch_ws reused workspace, rep {rep}")
+        check_layout_dispatch_ws(moe, idx, xb, E, P, C, 0, rep, f"rep {rep}", ws=ws)
+        ws.fill_(0xEE)
+
+
 def test_dispatch_all_masked_writes_nothing(moe):
     S, K, H = 8, 4, 64
     slot = np.full((S, K), -1, np.int32)
@@ -1125,7 +1217,8 @@ def test_maximum_tokens_and_channels(moe):
     assert np.array_equal(y, oracle.combine(rows, ref["slot_idx"], wts))
 
 
-@pytest.mark.parametrize("cfg,quant,fused", [(2, 0, True), (2, 1, True), (1, 2, True), (3, 0, False)])
+@pytest.mark.parametrize("cfg,quant,fused", [(2, 0, True), (2, 1, True), (1, 2, True), (3, 0, False), (3, 0, "ws"),
+                                             (2, 0, "ws")])
 def test_plans_match_the_oracle(moe, cfg, quant, fused):
     """Pre-validated calls (moe_plan_*, run by moe_plan_run) on fixed buffers, three seeded inputs
     copied into them one after the other: layout, window and y against the oracle each time."""
@@ -1138,9 +1231,15 @@ def test_plans_match_the_oracle(moe, cfg, quant, fused):
     lay = moe.empty_layout(S, K, E, P, C, DEV)
     win = torch.empty(moe.moe_window_bytes(S, K, H), dtype=torch.uint8, device=DEV)
     y = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
-    nws = moe.moe_dispatch_workspace_bytes(S, K, quant)
+    if fused == "ws":
+        nws = moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C, quant)
+    else:
+        nws = moe.moe_dispatch_workspace_bytes(S, K, quant)
     ws = torch.empty(nws, dtype=torch.uint8, device=DEV) if nws else None
-    if fused:
+    if fused == "ws":
+        plans = [moe.plan_layout_ws(idx_s, E, P, C, lay, ws, quant),
+                 moe.plan_dispatch_planned(x_s, lay.slot_idx, win, ws, C, quant, 6)]
+    elif fused:
         plans = [moe.plan_layout_dispatch(idx_s, E, P, C, x_s, win, lay, quant, 6)]
     else:
         plans = [moe.plan_layout(idx_s, E, P, C, lay), moe.plan_dispatch_ws(x_s, lay.slot_idx, win, ws, quant, 6)]
