@@ -1114,11 +1114,12 @@ def test_combine_row_stride_and_expert_rows(moe):
 # ---------------------------------------------------------------- determinism
 
 
-@pytest.mark.parametrize("cfg,quant,fused", [(3, 0, False), (3, 0, "ws"), (2, 0, False), (2, 0, True),
-                                             (2, 1, True), (1, 2, True)])
+@pytest.mark.parametrize("cfg,quant,fused", [(3, 0, False), (3, 0, "ws"), (3, 0, "lws"), (5, 0, "lws"),
+                                             (2, 0, False), (2, 0, True), (2, 1, True), (1, 2, True)])
 def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
     """Each kernel twice on identical inputs, outputs poisoned differently before each run: the
     three-launch layout (workload 3), the planned pack (workload 3, its workspace poisoned too), the
+    two-launch layout with the pack from its plan (workloads 3 and 5, workspace poisoned), the
     single-launch layout (workload 2) and the one-kernel layout + pack (moe_layout_dispatch)."""
     w = WORKLOADS[cfg]
     inp = inputs(cfg)
@@ -1133,7 +1134,12 @@ def test_repeat_runs_are_byte_identical(moe, cfg, quant, fused):
         for t in lay:
             t.view(torch.uint8).fill_(poison)
         win = torch.full((moe.moe_window_bytes(w.S, w.K, w.H),), poison, dtype=torch.uint8, device=DEV)
-        if fused == "ws":
+        if fused == "lws":
+            ws = torch.full((moe.moe_layout_dispatch_workspace_bytes(w.S, w.K, w.E, w.P, w.C, quant),), poison,
+                            dtype=torch.uint8, device=DEV)
+            moe.moe_layout_ws(idx, w.E, w.P, w.C, ws, quant, out=lay)
+            moe.moe_dispatch_planned(x, lay.slot_idx, win, ws, w.C, quant)
+        elif fused == "ws":
             moe.moe_layout(idx, w.E, w.P, w.C, out=lay)
             ws = torch.full((moe.moe_dispatch_workspace_bytes(w.S, w.K, quant),), poison, dtype=torch.uint8,
                             device=DEV)
@@ -1279,14 +1285,20 @@ def test_python_layer_rejects_bad_window(moe):
 # ---------------------------------------------------------------- graph capture
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fused", [False, True, "lws"])
 def test_step_replays_from_a_captured_graph(moe, fused):
-    """layout -> dispatch -> combine (or moe_layout_dispatch -> combine) captured once in a HIP
-    graph (the library allocates and synchronises nothing) and replayed on fresh inputs copied into
-    the captured buffers; every replay must equal the eager result on the same inputs. Eager work
-    runs between replays."""
-    w = WORKLOADS[1]
-    S, K, H, E, P, C = w.S, w.K, w.H, w.E, w.P, w.C
+    """layout -> dispatch -> combine (or moe_layout_dispatch -> combine, or moe_layout_ws ->
+    moe_dispatch_planned -> combine on a table of 8192 entries) captured once in a HIP graph (the
+    library allocates and synchronises nothing) and replayed on fresh inputs copied into the
+    captured buffers; every replay must equal the eager result on the same inputs. Eager work runs
+    between replays."""
+    if fused == "lws":
+        S, K, H, E, P, C = 1024, 8, 256, 64, 8, 32
+    else:
+        w = WORKLOADS[1]
+        S, K, H, E, P, C = w.S, w.K, w.H, w.E, w.P, w.C
+    lws = torch.empty(max(16, moe.moe_layout_dispatch_workspace_bytes(S, K, E, P, C)), dtype=torch.uint8,
+                      device=DEV)
     x_s = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
     idx_s = torch.empty((S, K), dtype=torch.int32, device=DEV)
     wts_s = torch.empty((S, K), dtype=torch.float32, device=DEV)
@@ -1304,7 +1316,10 @@ def test_step_replays_from_a_captured_graph(moe, fused):
         eo_s.copy_(bf16_dev(f32_to_bf16_input(rng.standard_normal((S * K, H)).astype(np.float32))))
 
     def step():
-        if fused:
+        if fused == "lws":
+            moe.moe_layout_ws(idx_s, E, P, C, lws, 0, out=lay_s)
+            moe.moe_dispatch_planned(x_s, lay_s.slot_idx, win_s, lws, C, 0)
+        elif fused:
             moe.moe_layout_dispatch(idx_s, E, P, C, x_s, win_s, 0, out=lay_s)
         else:
             moe.moe_layout(idx_s, E, P, C, out=lay_s)
@@ -1334,7 +1349,7 @@ def test_step_replays_from_a_captured_graph(moe, fused):
         step()  # eager reference on the same inputs
         torch.cuda.synchronize()
         ref = snapshot()
-        for t in (*lay_s, win_s, y_s):  # poison, then replay
+        for t in (*lay_s, win_s, y_s, lws):  # poison (the workspace too), then replay
             t.view(torch.uint8).fill_(0x5A)
         torch.cuda.synchronize()
         graph.replay()

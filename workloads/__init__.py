@@ -34,7 +34,7 @@ class Workload:
     outlier_prob: float = 0.0
     outlier_mul: float = 1.0
     zipf_s: Optional[float] = None
-    quant: int = 0  # 0 = bf16 slots, 1 = fp8 e4m3 dynamic quant
+    quant: int = 0  # 0 = bf16 slots, 1 = fp8 e4m3 dynamic quant, 2 = int8 dynamic quant
 
     @property
     def C(self):
@@ -42,7 +42,7 @@ class Workload:
         return min(self.S, 128)
 
     def describe(self):
-        q = "fp8-e4m3-dyn" if self.quant else "bf16"
+        q = {0: "bf16", 1: "fp8-e4m3-dyn", 2: "int8-dyn"}[self.quant]
         skew = f" zipf{self.zipf_s}" if self.zipf_s else ""
         return f"{self.name} S={self.S} H={self.H} E={self.E} P={self.P} K={self.K} {q}{skew}"
 
