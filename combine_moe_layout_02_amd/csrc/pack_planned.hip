@@ -112,10 +112,12 @@ __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const int lane = threadIdx.x;
     const int row_bytes = nvec << 4;
     if (m < npf) {
-        const int c = ((m >> pc.lt) << 3) + xcd;  // group
+        // last group first, so that the first groups stored are the ones fetched last (still in L2)
+        const int mr = npf - 1 - m;
+        const int c = ((mr >> pc.lt) << 3) + xcd;  // group
         const int tc0 = c * pc.a + min(c * pc.d, pc.b);
         const int tc1 = (c + 1) * pc.a + min((c + 1) * pc.d, pc.b);
-        const int t = tc0 + (m & ((1 << pc.lt) - 1));
+        const int t = tc0 + (mr & ((1 << pc.lt) - 1));
         if (c >= pc.nsub || t >= tc1 || t >= S) return;
         const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
         uint32_t acc = 0;
