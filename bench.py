@@ -8,11 +8,15 @@ timings, the roofline of the dominant kernel and the CPU oracle timed on the
 host cores as a reported baseline.
 
 The layout is moe_layout_ws (two kernels; in bf16 the second also writes the
-pack's plan into the workspace) and the dispatch moe_dispatch_planned (the
-planned pack kernel alone, reading that plan). extras.three_launch_layout_dispatch_ws
-times the step with moe_layout (three kernels) + moe_dispatch_ws (plan kernel +
-pack kernel), and the token-order moe_dispatch is timed in
-extras.dispatch_token_order.
+pack's plan into the workspace), the dispatch moe_dispatch_planned (the
+planned pack kernel alone, reading that plan) and the combine moe_combine, each
+checked once per input set into a pre-validated call (moe_plan_layout_ws,
+moe_plan_dispatch_planned, moe_plan_combine) and launched by one moe_plan_run:
+the same kernels as the Python calls without their per-call argument checks and
+marshalling, which extras.eager_binding_calls times.
+extras.three_launch_layout_dispatch_ws times the step with moe_layout (three
+kernels) + moe_dispatch_ws (plan kernel + pack kernel), and the token-order
+moe_dispatch is timed in extras.dispatch_token_order.
 
 Cache state: the timed steps cycle over --rotate (default 8) copies of the batch
 at distinct addresses, so each step reads its inputs from HBM rather than from
@@ -20,10 +24,10 @@ the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); ext
 one set of buffers. ceilings holds the library's own 1 GiB probes (write-only
 fill, read-only stream, copy); each kernel also reports its bandwidth against
 the ceiling of its own read/write mix, (r + w) / (r / read + w / fill).
-extras.fused_layout_dispatch times the same eager steps with the layout and the pack
-in one moe_layout_dispatch call (one kernel for decode-sized tables), and
-extras.planned_calls_eager the same step through pre-validated calls (moe_plan_*,
-checked once, then one moe_plan_run per launch).
+extras.fused_layout_dispatch times the step with the layout and the pack in one
+moe_layout_dispatch call (one kernel for decode-sized tables) through the
+binding, and at decode sizes extras.plans_fused_layout_dispatch the same two
+calls as pre-validated calls.
 extras.graph_replay times the same step captured in HIP graphs (one per input
 set): the device time per step without Python's launch overhead, which is what
 bounds the event timings at decode sizes. extras.graph_replay_fused_layout_dispatch
@@ -246,18 +250,32 @@ def time_three_launch_eager(args, torch, moe, w, C, sets, lay, window, y, total_
             "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
-def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes, lws):
-    """The step through pre-validated calls (moe_plan_*): one plan per input set made once, then each
-    step runs its plans (moe_plan_run: one short C call per launch, no argument checks), launched
-    eagerly like the timed steps."""
-    plans = []
-    for x, topk, wts, eo in sets:
-        if w.S * w.K <= 4096 and C <= 1024:  # decode sizes: layout + pack in one kernel
-            first = [moe.plan_layout_dispatch(topk, w.E, w.P, C, x, window, lay, w.quant, 0)]
-        else:
-            first = [moe.plan_layout_ws(topk, w.E, w.P, C, lay, lws, w.quant),
-                     moe.plan_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)]
-        plans.append([p.run for p in first] + [moe.plan_combine(eo, lay.slot_idx, wts, y).run])
+def time_eager_binding(args, torch, moe, w, C, sets, lay, window, y, total_bytes, lws):
+    """The step's three calls through the Python binding (moe_layout_ws, moe_dispatch_planned,
+    moe_combine: argument checks and marshalling on every call), launched like the timed steps."""
+    def step(i):
+        x, topk, wts, eo = sets[i % len(sets)]
+        moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
+        moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
+        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
+
+
+def time_plans_fused(args, torch, moe, w, C, sets, lay, window, y, total_bytes):
+    """Decode sizes: the step as two pre-validated calls, the one-kernel layout + pack
+    (moe_plan_layout_dispatch) and the combine, launched like the timed steps."""
+    plans = [[moe.plan_layout_dispatch(topk, w.E, w.P, C, x, window, lay, w.quant, 0).run,
+              moe.plan_combine(eo, lay.slot_idx, wts, y).run] for x, topk, wts, eo in sets]
     n = len(plans)
     for i in range(args.warmup):
         for run in plans[i % n]:
@@ -270,7 +288,7 @@ def time_planned_eager(args, torch, moe, w, C, sets, lay, window, y, total_bytes
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / args.steps
     return {"ms_per_step": round(ms, 4), "value": round(total_bytes / (ms * 1e-3) / 1e9, 1),
-            "tokens_per_s": round(w.S / (ms * 1e-3), 1), "launch_calls_per_step": len(plans[0])}
+            "tokens_per_s": round(w.S / (ms * 1e-3), 1)}
 
 
 def time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=False, per_graph=1,
@@ -474,7 +492,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 100 warm-up steps (about 18 ms at workload 3): with 10 the first timed steps still run 1-2% slower
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--channels", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=8,
@@ -541,11 +560,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the step's three calls, checked once per input set (moe_plan_*); each launch is one moe_plan_run
+    plans = {}
+
+    def plans_of(st):
+        key = id(st[0])
+        if key not in plans:
+            x, topk, wts, eo = st
+            plans[key] = (moe.plan_layout_ws(topk, w.E, w.P, C, lay, lws, w.quant).run,
+                          moe.plan_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0).run,
+                          moe.plan_combine(eo, lay.slot_idx, wts, y).run)
+        return plans[key]
+
+    for st in sets:
+        plans_of(st)
+
     def step(i, sets_used):
-        x, topk, wts, eo = sets_used[i % len(sets_used)]
-        moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
-        moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
-        moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+        layout, dispatch, combine = plans_of(sets_used[i % len(sets_used)])
+        layout()
+        dispatch()
+        combine()
 
     def timed(sets_used):
         """W untimed then K timed steps cycling over sets_used, timed by the wall clock between two
@@ -565,13 +599,13 @@ def main():
         t1 = time.perf_counter()
         for i in range(args.steps):
             e = ev[i]
-            x, topk, wts, eo = sets_used[i % len(sets_used)]
+            layout, dispatch, combine = plans_of(sets_used[i % len(sets_used)])
             e[0].record(stream)
-            moe.moe_layout_ws(topk, w.E, w.P, C, lws, w.quant, out=lay)
+            layout()
             e[1].record(stream)
-            moe.moe_dispatch_planned(x, lay.slot_idx, window, lws, C, w.quant, 0)
+            dispatch()
             e[2].record(stream)
-            moe.moe_combine(eo, lay.slot_idx, wts, y=y)
+            combine()
             e[3].record(stream)
         torch.cuda.synchronize()
         elapsed_events = time.perf_counter() - t1
@@ -627,9 +661,9 @@ def main():
         return out
 
     calls = {
-        "layout": lambda st: moe.moe_layout_ws(st[1], w.E, w.P, C, lws, w.quant, out=lay),
-        "dispatch": lambda st: moe.moe_dispatch_planned(st[0], lay.slot_idx, window, lws, C, w.quant, 0),
-        "combine": lambda st: moe.moe_combine(st[3], lay.slot_idx, st[2], y=y),
+        "layout": lambda st: plans_of(st)[0](),
+        "dispatch": lambda st: plans_of(st)[1](),
+        "combine": lambda st: plans_of(st)[2](),
     }
 
     nbytes = algorithmic_bytes(w, C, n_valid)
@@ -708,13 +742,16 @@ def main():
                                                                   y, total_bytes)
         out["extras"]["three_launch_layout_dispatch_ws"] = time_three_launch_eager(
             args, torch, moe, w, C, sets, lay, window, y, total_bytes, ws)
-        out["extras"]["planned_calls_eager"] = time_planned_eager(args, torch, moe, w, C, sets, lay, window, y,
+        out["extras"]["eager_binding_calls"] = time_eager_binding(args, torch, moe, w, C, sets, lay, window, y,
                                                                   total_bytes, lws)
         out["extras"]["graph_replay"] = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y,
                                                           total_bytes, lws=lws)
         fused = time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes, fused=True)
         fused["one_kernel_layout_dispatch"] = w.S * w.K <= 4096 and C <= 1024
         out["extras"]["graph_replay_fused_layout_dispatch"] = fused
+        if w.S * w.K <= 4096 and C <= 1024:  # decode sizes: the one-kernel layout + pack as a plan
+            out["extras"]["plans_fused_layout_dispatch"] = time_plans_fused(args, torch, moe, w, C, sets, lay,
+                                                                            window, y, total_bytes)
         if w.S * w.K <= 4096:  # decode sizes: 16 steps per graph, the replay's own cost shared
             out["extras"]["graph_replay_16_steps_per_graph"] = {
                 "separate": time_graph_replay(args, torch, moe, w, C, sets, lay, window, y, total_bytes,
