@@ -500,13 +500,13 @@ int moe_layout_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int3
 
 int moe_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                          int32_t C, int32_t quant, int32_t src_rank, void *window,
-                         int64_t window_bytes, const void *workspace, int64_t workspace_bytes,
+                         int64_t window_bytes, void *workspace, int64_t workspace_bytes,
                          hipStream_t stream) {
     const int st = check_dispatch_planned(x, slot_idx, S, H, K, C, quant, window, window_bytes,
                                           workspace, workspace_bytes);
     if (st != MOE_OK) return st;
-    return run_dispatch_planned(x, slot_idx, S, H, K, C, quant, src_rank, window,
-                                const_cast<void *>(workspace), stream);
+    return run_dispatch_planned(x, slot_idx, S, H, K, C, quant, src_rank, window, workspace,
+                                stream);
 }
 
 int moe_layout_dispatch_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
@@ -613,13 +613,13 @@ int moe_plan_layout_ws(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32
 
 int moe_plan_dispatch_planned(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
                               int32_t H, int32_t K, int32_t C, int32_t quant, int32_t src_rank,
-                              void *window, int64_t window_bytes, const void *workspace,
+                              void *window, int64_t window_bytes, void *workspace,
                               int64_t workspace_bytes) {
     if (!plan) return MOE_ERR_ARG;
     PlanRecord rec{};
     rec.kind = PlanRecord::kDispatchPlanned;
-    rec.dispatch_planned = DispatchPlannedArgs{x, slot_idx, S, H, K, C, quant, src_rank, window,
-                                               const_cast<void *>(workspace)};
+    rec.dispatch_planned =
+        DispatchPlannedArgs{x, slot_idx, S, H, K, C, quant, src_rank, window, workspace};
     return store_plan(plan, rec,
                       check_dispatch_planned(x, slot_idx, S, H, K, C, quant, window, window_bytes,
                                              workspace, workspace_bytes));

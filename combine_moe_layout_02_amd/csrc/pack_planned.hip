@@ -96,11 +96,11 @@ __global__ __launch_bounds__(kPlanThreads) void pack_plan_kernel(const int32_t *
 }
 
 // grid = 8 * (nsx * 2^lt + nsx * cap * nparts) workgroups of kPartLanes. Workgroup b: XCD
-// x = b % 8, index m = b / 8 in that XCD's sequence: m < nsx * 2^lt reads token m & (2^lt - 1) of
-// group 8(m >> lt) + x (if the group has that many) and stores nothing; otherwise record
-// (m - nsx * 2^lt) / nparts of list x, part (m - nsx * 2^lt) % nparts (the quotient by a multiply-high with np_magic = ceil(2^32 / nparts),
-// exact for nparts in [2, 32] and indices below 2^24; nparts = 1 needs no division and its
-// magic, 2^32, would not fit in 32 bits).
+// x = b % 8, index m = b / 8 in that XCD's sequence: m < nsx * 2^lt, with r = nsx * 2^lt - 1 - m,
+// reads token r & (2^lt - 1) of group 8(r >> lt) + x (if the group has that many) and stores
+// nothing; otherwise record (m - nsx * 2^lt) / nparts of list x, part (m - nsx * 2^lt) % nparts.
+// The quotient is a multiply-high with np_magic = ceil(2^32 / nparts), exact for nparts in [2, 32]
+// and indices below 2^24; nparts = 1 needs no division (its magic, 2^32, would not fit in 32 bits).
 __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const uint8_t *__restrict__ x, const int2 *__restrict__ plan, int S, int K, int nvec,
     int nparts, uint32_t np_magic, PackChunks pc, SlotGeom g, int src_rank,

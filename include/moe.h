@@ -263,7 +263,8 @@ int moe_layout_dispatch_ex(const int32_t *topk_idx, int32_t S, int32_t K, int32_
  *      that moe_layout_ws call, and the workspace must not have been written in between (a plan from
  *      another table writes that table's bytes; records are bounds-checked, so never outside the
  *      window or x). Where the layout writes no plan, the call runs moe_dispatch_ws's plan kernel on
- *      slot_idx (bf16, S*K >= 8192) or the token-order pack (no workspace needed). Checks: those of
+ *      slot_idx (bf16, S*K >= 8192; it writes the workspace's plan part) or the token-order pack (no
+ *      workspace needed). Checks: those of
  *      moe_dispatch, C in [1, min(S, MOE_MAX_CHANNELS)], then the workspace as above, against the plan's
  *      part only. Enqueues 1 kernel (2 when it runs the plan kernel).
  * moe_layout_dispatch_ws: moe_layout_dispatch_ex's arguments plus the workspace: moe_layout_ws then
@@ -281,7 +282,7 @@ int moe_layout_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int3
 
 int moe_dispatch_planned(const void *x, const int32_t *slot_idx, int32_t S, int32_t H, int32_t K,
                          int32_t C, int32_t quant, int32_t src_rank, void *window,
-                         int64_t window_bytes, const void *workspace, int64_t workspace_bytes,
+                         int64_t window_bytes, void *workspace, int64_t workspace_bytes,
                          hipStream_t stream);
 
 int moe_layout_dispatch_ws(const int32_t *topk_idx, int32_t S, int32_t K, int32_t E, int32_t P,
@@ -500,7 +501,7 @@ int moe_plan_layout_ws(moe_plan *plan, const int32_t *topk_idx, int32_t S, int32
                        int32_t path, void *workspace, int64_t workspace_bytes);
 int moe_plan_dispatch_planned(moe_plan *plan, const void *x, const int32_t *slot_idx, int32_t S,
                               int32_t H, int32_t K, int32_t C, int32_t quant, int32_t src_rank,
-                              void *window, int64_t window_bytes, const void *workspace,
+                              void *window, int64_t window_bytes, void *workspace,
                               int64_t workspace_bytes);
 int moe_plan_run(const moe_plan *plan, hipStream_t stream);
 
