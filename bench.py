@@ -23,7 +23,8 @@ at distinct addresses, so each step reads its inputs from HBM rather than from
 the 256 MB memory-side cache (eight copies of x alone are 470 MB at S=4096); extras.warm_same_buffers repeats the timing with
 one set of buffers. ceilings holds the library's own 1 GiB probes (write-only
 fill, read-only stream, copy); each kernel also reports its bandwidth against
-the ceiling of its own read/write mix, (r + w) / (r / read + w / fill).
+the ceiling of its own read/write mix, (r + w) / (r / read + w / fill), and
+against the measured copy (frac_copy_ceiling).
 extras.fused_layout_dispatch times the step with the layout and the pack in one
 moe_layout_dispatch call (one kernel for decode-sized tables) through the
 binding, and at decode sizes extras.plans_fused_layout_dispatch the same two
@@ -632,6 +633,8 @@ def main():
             pc = pattern_ceilings.get(k)
             if pc:
                 kernels[k]["frac_pattern_ceiling"] = round(gbs / pc, 4)
+            if ceil:
+                kernels[k]["frac_copy_ceiling"] = round(gbs / ceil["copy"], 4)
         return kernels, 1e3 * elapsed / args.steps, 1e3 * elapsed_events / args.steps
 
     def isolated(sets_used, calls):
