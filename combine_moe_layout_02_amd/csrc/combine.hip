@@ -9,7 +9,7 @@
 //
 // Each token row is split into parts of 32 16-byte vectors and one half-wave workgroup owns one
 // (token, part): each lane issues its K gathered 16-byte loads back to back, then reduces them and
-// stores one 16-byte vector of y. Measured on MI355X at S=4096..8192, H=7168, K=8, 32-lane parts
+// stores one 16-byte vector of y. All parts of a token run on one XCD. Measured on MI355X at S=4096..8192, H=7168, K=8, 32-lane parts
 // are 1-3% faster than 64- or 128-lane parts and 16-lane parts a third slower. Slots and weights
 // are uniform per workgroup and live in scalar registers. The gathered rows are read exactly once,
 // so they are loaded with the non-temporal policy and do not displace reusable data from the
@@ -41,15 +41,22 @@ __device__ inline uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// grid = S * nparts; workgroup (t, q) produces vectors [q, q + 1) * kPartThreads of y[t]. STAGED:
-// the rows were first scattered to position t*K + k, so row t*K + k is read for every valid k.
+// grid = 8 * ceil(S / 8) * nparts; workgroup b runs on XCD x = b % 8 (the dispatcher hands
+// workgroups to the XCDs in turn) and produces vectors [q, q + 1) * kPartThreads of y[t], with
+// m = b / 8, t = 8 * (m / nparts) + x and q = m % nparts: all parts of token t on XCD t % 8, so each
+// XCD writes whole rows of y (about 1% faster than token-major order at S = 4096..8192, H = 7168).
+// STAGED: the rows were first scattered to position t*K + k, so row t*K + k is read for every
+// valid k.
 template <int KMAX, bool STAGED>
 __global__ __launch_bounds__(kPartThreads) void combine_kernel(
     const uint8_t *__restrict__ expert_out, int64_t stride, int64_t rows,
-    const int32_t *__restrict__ slot_idx, const float *__restrict__ weights, int K, int nvec,
-    int nparts, uint8_t *__restrict__ y) {
-    const int t = blockIdx.x / nparts;
-    const int q = blockIdx.x - t * nparts;
+    const int32_t *__restrict__ slot_idx, const float *__restrict__ weights, int S, int K,
+    int nvec, int nparts, uint8_t *__restrict__ y) {
+    const int m = blockIdx.x >> 3;
+    const int i = m / nparts;
+    const int q = m - i * nparts;
+    const int t = 8 * i + (blockIdx.x & 7);
+    if (t >= S) return;
     const int v = q * kPartThreads + threadIdx.x;
     const int row_bytes = nvec << 4;
     __amdgpu_buffer_rsrc_t src[KMAX];
@@ -125,9 +132,10 @@ template <int KMAX, bool STAGED>
 hipError_t launch(const void *expert_out, int64_t stride, int64_t rows, const int32_t *slot_idx,
                   const float *weights, int S, int K, int nvec, void *y, hipStream_t stream) {
     const int nparts = (nvec + kPartThreads - 1) / kPartThreads;
-    hipLaunchKernelGGL((combine_kernel<KMAX, STAGED>), dim3((uint32_t)S * nparts),
-                       dim3(kPartThreads), 0, stream, static_cast<const uint8_t *>(expert_out),
-                       stride, rows, slot_idx, weights, K, nvec, nparts, static_cast<uint8_t *>(y));
+    const uint32_t grid = 8u * (uint32_t)((S + 7) / 8) * (uint32_t)nparts;
+    hipLaunchKernelGGL((combine_kernel<KMAX, STAGED>), dim3(grid), dim3(kPartThreads), 0, stream,
+                       static_cast<const uint8_t *>(expert_out), stride, rows, slot_idx, weights, S,
+                       K, nvec, nparts, static_cast<uint8_t *>(y));
     return hipGetLastError();
 }
 
