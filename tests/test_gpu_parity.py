@@ -611,6 +611,18 @@ def test_layout_dispatch_ws_shapes(moe, case):
     check_layout_dispatch_ws(moe, idx, xb, E, P, C, quant, seed, str(case), path=1, split=seed % 2 == 0)
 
 
+def test_layout_ws_at_the_maxima(moe):
+    """moe_layout_ws + moe_dispatch_planned at S = MOE_MAX_TOKENS, K = MOE_MAX_K, E = MOE_MAX_EXPERTS and
+    C = MOE_MAX_CHANNELS (16 tokens a channel: the layout writes 64 groups of 4 channels per XCD list),
+    with masked and bad ids: every layout output and the window equal to the oracle's."""
+    rng = np.random.default_rng(301)
+    S, K, E, P, C, H = 65536, 16, 512, 256, 4096, 16  # the header's MOE_MAX_* limits
+    idx = random_tiny_routing(rng, S, K, E, p_mask=0.02, p_bad=0.001)
+    xb = f32_to_bf16_input(rng.standard_normal((S, H)).astype(np.float32))
+    note("layout_ws at the maxima")
+    check_layout_dispatch_ws(moe, idx, xb, E, P, C, 0, 5, "maxima", split=True)
+
+
 def test_layout_dispatch_ws_reused_workspace(moe):
     """Two tables through one workspace, the second after the workspace was overwritten, and the
     first again: every output equal to the oracle's each time."""
