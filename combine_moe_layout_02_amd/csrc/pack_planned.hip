@@ -21,9 +21,9 @@
 // moe_layout_ws can write the record lists itself (groups of whole channels instead of token chunks;
 // the PackChunks argument says which), and the pack kernel then runs alone (moe_dispatch_planned).
 //
-// Measured at S=4096, H=7168, K=8 with x in HBM: 82 us for the pack kernel and 3.4 us for the plan,
-// against 100 us for the token-order pack; at S=8192, P=128 with Zipf routing 173 + 3.6 us against
-// 194 us. The pack kernel's prologue holds no runtime integer division (a 32-bit multiply-high
+// Measured at S=4096, H=7168, K=8 with x in HBM: 83 us for the pack kernel (and 3.4 us for the plan
+// kernel when the layout does not write the lists), against 98 us for the token-order pack; at
+// S=8192, P=128 with Zipf routing 170-187 us against 193 us. The pack kernel's prologue holds no runtime integer division (a 32-bit multiply-high
 // replaces the division by the part count): with divisions the same kernel took 117 us, because
 // the pack is bound by how fast workgroups turn over.
 //
