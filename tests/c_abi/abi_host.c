@@ -37,6 +37,24 @@ int main(void) {
           "moe_layout_dispatch rejects a small window");
     check(moe_combine(dev, 14336, 512, dev, dev, 64, 7168, 8, (char *)dev + 8, NULL) == MOE_ERR_ALIGN,
           "moe_combine rejects a misaligned y");
+    {
+        const int64_t ws = moe_layout_dispatch_workspace_bytes(4096, 8, 256, 8, 128, MOE_QUANT_NONE, MOE_LAYOUT_AUTO);
+        moe_plan plan;
+        memset(&plan, 0, sizeof(plan));
+        check(ws == 525312, "moe_layout_dispatch_workspace_bytes at S=4096, C=128");
+        check(moe_layout_dispatch_workspace_bytes(64, 8, 256, 8, 16, MOE_QUANT_NONE, MOE_LAYOUT_AUTO) == 0,
+              "no workspace for a table the single kernel takes");
+        check(moe_layout_ws(dev, 4096, 8, 256, 8, 128, dev, dev, dev, dev, dev, dev, dev, dev, dev, MOE_QUANT_NONE,
+                            MOE_LAYOUT_AUTO, dev, ws - 1, NULL) == MOE_ERR_WINDOW,
+              "moe_layout_ws rejects a short workspace");
+        check(moe_dispatch_planned(dev, dev, 4096, 7168, 8, 128, MOE_QUANT_NONE, 0, dev,
+                                   moe_window_bytes(4096, 8, 7168), NULL, 0, NULL) == MOE_ERR_ARG,
+              "moe_dispatch_planned needs the workspace for a planned table");
+        check(moe_plan_layout_ws(&plan, dev, 4096, 8, 256, 8, 128, dev, dev, dev, dev, dev, dev, dev, dev, dev,
+                                 MOE_QUANT_NONE, MOE_LAYOUT_AUTO, NULL, ws) == MOE_ERR_ARG &&
+                  moe_plan_run(&plan, NULL) == MOE_ERR_ARG,
+              "a plan that failed its checks is refused");
+    }
     check(strlen(moe_status_string(MOE_ERR_WINDOW)) > 0, "moe_status_string");
     printf("%d failure(s)\n", failures);
     return failures ? 1 : 0;
