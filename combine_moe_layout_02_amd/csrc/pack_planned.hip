@@ -13,7 +13,7 @@
 //         workgroup scan, and the (slot, token, k) records are written in bucket order to the
 //         chunk's position in the list of the XCD that owns it (chunk c belongs to XCD c % 8).
 //   pack  one 128-lane workgroup per (record, 2 KB part of the row), preceded by one workgroup per
-//         row of the XCD's chunks that only reads the row. Workgroup b runs on XCD b % 8 (the
+//         2 KB part of each row of the XCD's chunks that only reads it. Workgroup b runs on XCD b % 8 (the
 //         dispatcher hands out workgroups to the eight XCDs in turn), so each XCD first brings its
 //         rows into its L2 and the memory-side cache, then stores its records in slot order:
 //         consecutive workgroups write neighbouring slots, and the K re-reads of a row hit cache.
@@ -95,12 +95,13 @@ __global__ __launch_bounds__(kPlanThreads) void pack_plan_kernel(const int32_t *
     if (tid >= total && tid < TcK) out[tid] = int2{-1, 0};
 }
 
-// grid = 8 * (nsx * 2^lt + nsx * cap * nparts) workgroups of kPartLanes. Workgroup b: XCD
-// x = b % 8, index m = b / 8 in that XCD's sequence: m < nsx * 2^lt, with r = nsx * 2^lt - 1 - m,
-// reads token r & (2^lt - 1) of group 8(r >> lt) + x (if the group has that many) and stores
-// nothing; otherwise record (m - nsx * 2^lt) / nparts of list x, part (m - nsx * 2^lt) % nparts.
-// The quotient is a multiply-high with np_magic = ceil(2^32 / nparts), exact for nparts in [2, 32]
-// and indices below 2^24; nparts = 1 needs no division (its magic, 2^32, would not fit in 32 bits).
+// grid = 8 * (nsx * 2^lt * nparts + nsx * cap * nparts) workgroups of kPartLanes. Workgroup b: XCD
+// x = b % 8, index m = b / 8 in that XCD's sequence. m < nsx * 2^lt * nparts: with i = m / nparts
+// and r = nsx * 2^lt - 1 - i, reads part m % nparts of token r & (2^lt - 1) of group 8(r >> lt) + x
+// (if the group has that many) and stores nothing. Otherwise record (m - npf) / nparts of list x,
+// part (m - npf) % nparts. The quotients are a multiply-high with np_magic = ceil(2^32 / nparts),
+// exact for nparts in [2, 32] and indices below 2^24; nparts = 1 needs no division (its magic,
+// 2^32, would not fit in 32 bits).
 __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const uint8_t *__restrict__ x, const int2 *__restrict__ plan, int S, int K, int nvec,
     int nparts, uint32_t np_magic, PackChunks pc, SlotGeom g, int src_rank,
@@ -108,21 +109,23 @@ __global__ __launch_bounds__(kPartLanes) void pack_planned_kernel(
     const int b = blockIdx.x;
     const int xcd = b & 7;
     const int m = b >> 3;
-    const int npf = pc.nsx << pc.lt;
+    const int nrows = pc.nsx << pc.lt;
+    const int npf = nrows * nparts;
     const int lane = threadIdx.x;
     const int row_bytes = nvec << 4;
     if (m < npf) {
-        // last group first, so that the first groups stored are the ones fetched last (still in L2)
-        const int mr = npf - 1 - m;
+        // one workgroup per (row, part); last group first, so that the first groups stored are the
+        // ones fetched last (still in L2)
+        const uint32_t row = nparts == 1 ? (uint32_t)m : __umulhi((uint32_t)m, np_magic);
+        const int q = m - (int)row * nparts;
+        const int mr = nrows - 1 - (int)row;
         const int c = ((mr >> pc.lt) << 3) + xcd;  // group
         const int tc0 = c * pc.a + min(c * pc.d, pc.b);
         const int tc1 = (c + 1) * pc.a + min((c + 1) * pc.d, pc.b);
         const int t = tc0 + (mr & ((1 << pc.lt) - 1));
         if (c >= pc.nsub || t >= tc1 || t >= S) return;
-        const __amdgpu_buffer_rsrc_t src = rsrc(x + (int64_t)t * row_bytes, row_bytes);
-        uint32_t acc = 0;
-        for (int q = 0; q < nparts; ++q) acc ^= load16(src, (q * kPartLanes + lane) << 4).x;
-        asm volatile("" ::"v"(acc));  // keep the loads: they exist to fill the caches
+        const uint32_t v = load16(rsrc(x + (int64_t)t * row_bytes, row_bytes), (q * kPartLanes + lane) << 4).x;
+        asm volatile("" ::"v"(v));  // keep the load: it exists to fill the caches
         return;
     }
     const uint32_t mp = (uint32_t)(m - npf);
@@ -150,7 +153,7 @@ hipError_t launch_pack_from_plan(const void *x, const void *plan, const PackChun
     const int nvec = H / 8;
     const int nparts = (nvec + kPartLanes - 1) / kPartLanes;
     const uint32_t magic = nparts > 1 ? (uint32_t)((0x100000000ull + nparts - 1) / nparts) : 0u;
-    const int64_t nwg = 8 * (((int64_t)pc.nsx << pc.lt) + (int64_t)pc.nsx * pc.cap * nparts);
+    const int64_t nwg = 8 * (((int64_t)pc.nsx << pc.lt) * nparts + (int64_t)pc.nsx * pc.cap * nparts);
     hipLaunchKernelGGL(pack_planned_kernel, dim3((uint32_t)nwg), dim3(kPartLanes), 0, stream,
                        static_cast<const uint8_t *>(x), static_cast<const int2 *>(plan), S, K, nvec,
                        nparts, magic, pc, g, src_rank, static_cast<uint8_t *>(window));
